@@ -1,0 +1,214 @@
+"""ctypes wrapper around ``liboracle.so`` (built from ``trace_oracle.c``).
+
+Test infrastructure only: see the package docstring.  Arrays are numpy; bf16
+tensors travel as ``uint16`` bit patterns.  Every function mirrors one C
+function, whose comment cites the passage of the pages it follows.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "trace_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11", "-Wall"]
+
+
+def build(force=True):
+    """Compile the oracle with gcc (plain C, no vector intrinsics)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, f32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+        vp, u8 = ctypes.c_void_p, ctypes.c_uint8
+        sig = {
+            "oracle_e2m1_value": (f64, [i32]),
+            "oracle_e4m3_value": (f64, [i32]),
+            "oracle_e4m3_encode": (u8, [f32]),
+            "oracle_rtn_index": (i32, [f32]),
+            "oracle_rtn_nibble": (i32, [f32]),
+            "oracle_f32_to_bf16": (ctypes.c_uint16, [f32]),
+            "oracle_bf16_to_f32": (f32, [ctypes.c_uint16]),
+            "oracle_guided_nibble": (i32, [f32, i32, i32]),
+            "oracle_fullcode_nibble": (i32, [f32, i32]),
+            "oracle_dequant": (f32, [i32, u8, f32]),
+            "oracle_bitplane_offset": (i64, [i64]),
+            "oracle_guidance_bytes": (i64, [i64, i32]),
+            "oracle_amax": (i32, [vp, i64, i32, vp]),
+            "oracle_quant_rollout": (None, [vp, i64, i32, vp, i32, i64, i64, vp, vp, vp]),
+            "oracle_guidance_pack": (None, [vp, vp, i64, i32, i64, i64, vp]),
+            "oracle_fakequant_guided": (None, [vp, i64, i32, vp, vp, i32, i64, i64, vp, i32, vp]),
+            "oracle_fakequant_fullcode": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp]),
+            "oracle_fakequant_rtn": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+# ---- scalar helpers ------------------------------------------------------
+def e2m1_value(nibble):
+    return lib().oracle_e2m1_value(int(nibble))
+
+
+def e4m3_value(code):
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(t):
+    return int(lib().oracle_e4m3_encode(float(t)))
+
+
+def rtn_index(v):
+    return lib().oracle_rtn_index(float(v))
+
+
+def rtn_nibble(v):
+    return lib().oracle_rtn_nibble(float(v))
+
+
+def f32_to_bf16(f):
+    return int(lib().oracle_f32_to_bf16(float(f)))
+
+
+def bf16_to_f32(h):
+    return float(lib().oracle_bf16_to_f32(int(h)))
+
+
+def guided_nibble(v, k, gb):
+    return lib().oracle_guided_nibble(float(v), int(k), int(gb))
+
+
+def fullcode_nibble(v, r):
+    return lib().oracle_fullcode_nibble(float(v), int(r))
+
+
+def dequant(nibble, s, g):
+    return float(lib().oracle_dequant(int(nibble), int(s), float(g)))
+
+
+# ---- sizes ---------------------------------------------------------------
+def bitplane_offset(n):
+    return int(lib().oracle_bitplane_offset(int(n)))
+
+
+def guidance_bytes(n, k):
+    return int(lib().oracle_guidance_bytes(int(n), int(k)))
+
+
+# ---- tensor functions (full tensor in, blocks [b0, b1) processed) --------
+def amax(x, G=1):
+    """Global scale per group: returns (g float32[G], status)."""
+    x = _u16(x).reshape(-1)
+    g = np.zeros(G, np.float32)
+    st = lib().oracle_amax(_p(x), x.size, G, _p(g))
+    return g, st
+
+
+def _range(n, b0, b1):
+    return (0 if b0 is None else b0), (n // 16 if b1 is None else b1)
+
+
+def quant_rollout(y, g, k, G=1, b0=None, b1=None, guidance=True, out=None):
+    """RTN quantisation: returns (codes u8[n/2], scales u8[n/16], guidance u8 or None)."""
+    y = _u16(y).reshape(-1)
+    n = y.size
+    g = np.ascontiguousarray(g, np.float32)
+    b0, b1 = _range(n, b0, b1)
+    if out is None:
+        codes = np.zeros(n // 2, np.uint8)
+        scales = np.zeros(n // 16, np.uint8)
+        gd = np.zeros(guidance_bytes(n, k), np.uint8) if guidance else None
+    else:
+        codes, scales, gd = out
+    lib().oracle_quant_rollout(_p(y), n, G, _p(g), k, b0, b1, _p(codes), _p(scales), _p(gd))
+    return codes, scales, gd
+
+
+def guidance_pack(codes, scales, n, k, b0=None, b1=None, out=None):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    b0, b1 = _range(n, b0, b1)
+    gd = np.zeros(guidance_bytes(n, k), np.uint8) if out is None else out
+    lib().oracle_guidance_pack(_p(codes), _p(scales), n, k, b0, b1, _p(gd))
+    return gd
+
+
+def _outbufs(n, out_f32, want_codes):
+    y = np.zeros(n, np.float32 if out_f32 else np.uint16)
+    c = np.zeros(n // 2, np.uint8) if want_codes else None
+    return y, c
+
+
+def fakequant_guided(x, g, guidance, k, G=1, out_f32=False, b0=None, b1=None, codes=True):
+    x = _u16(x).reshape(-1)
+    n = x.size
+    g = np.ascontiguousarray(g, np.float32)
+    gd = np.ascontiguousarray(guidance, np.uint8)
+    b0, b1 = _range(n, b0, b1)
+    y, c = _outbufs(n, out_f32, codes)
+    lib().oracle_fakequant_guided(_p(x), n, G, _p(g), _p(gd), k, b0, b1, _p(y), int(out_f32), _p(c))
+    return y, c
+
+
+def fakequant_fullcode(x, g, guidance, G=1, out_f32=False, b0=None, b1=None, codes=True):
+    x = _u16(x).reshape(-1)
+    n = x.size
+    g = np.ascontiguousarray(g, np.float32)
+    gd = np.ascontiguousarray(guidance, np.uint8)
+    b0, b1 = _range(n, b0, b1)
+    y, c = _outbufs(n, out_f32, codes)
+    lib().oracle_fakequant_fullcode(_p(x), n, G, _p(g), _p(gd), b0, b1, _p(y), int(out_f32), _p(c))
+    return y, c
+
+
+def fakequant_rtn(x, g, scales_in=None, G=1, out_f32=False, b0=None, b1=None, codes=True):
+    """Plain RTN fake-quant: returns (y, codes or None, scales used)."""
+    x = _u16(x).reshape(-1)
+    n = x.size
+    g = np.ascontiguousarray(g, np.float32)
+    sin = None if scales_in is None else np.ascontiguousarray(scales_in, np.uint8)
+    b0, b1 = _range(n, b0, b1)
+    y, c = _outbufs(n, out_f32, codes)
+    sout = np.zeros(n // 16, np.uint8)
+    lib().oracle_fakequant_rtn(_p(x), n, G, _p(g), _p(sin), b0, b1, _p(y), int(out_f32), _p(c), _p(sout))
+    return y, c, sout
+
+
+def unpack_nibbles(codes):
+    """u8[n/2] -> u8[n] (element 2m in the low nibble)."""
+    codes = np.asarray(codes, np.uint8)
+    out = np.empty(codes.size * 2, np.uint8)
+    out[0::2] = codes & 0xF
+    out[1::2] = codes >> 4
+    return out
