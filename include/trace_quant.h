@@ -1,0 +1,149 @@
+/*
+ * trace_quant.h -- C ABI of the rollout-guided FP4 (E2M1) fake-quant library
+ * for MI355X (gfx950).  Library: libtrace_quant.so.
+ *
+ * The method (TRACE: Rollout-Guided Quantization-Aware Training for FP4
+ * Reinforcement Learning of MoE Language Models) is described on the page
+ * "Alibaba Qwen Proposes TRACE for 5.4x Faster FP4 RL Rollouts":
+ *   - section "Why Does FP4 Rollout 'Break' RL Training?", Figure 1 and its
+ *     worked example: both sides apply the same global scale and block scale,
+ *     then round to FP4; a tiny difference across a rounding boundary becomes
+ *     one whole codebook step;
+ *   - section "TRACE Core Concept", Figure 3: the rollout side records the FP4
+ *     results of routed-expert activations and KV states; the training side's
+ *     fake quantisation still picks one of the two adjacent E2M1 points, but
+ *     the one nearer the rollout's actual code rather than plain RTN; what is
+ *     kept is the scale plus a little mantissa information, because nearly
+ *     all mismatches are a single adjacent codebook entry.
+ *
+ * Conventions this library fixes where the pages are silent:
+ *   - blocks of 16 consecutive elements; one E4M3 block scale per block
+ *     (round to nearest even, saturating at 448, subnormals kept); one FP32
+ *     global scale per group of consecutive elements, g = amax / 2688
+ *     (2688 = 6 * 448), G groups of equal size (G = 1: one per tensor);
+ *   - fp32 scale chain, IEEE round-to-nearest-even, no fused operations:
+ *     t = a_b / (6 g); s = E4M3(t); c = s * g; inv = 1 / c (0 if c == 0,
+ *     FLT_MAX if 1 / c overflows); v = x * inv;
+ *   - RTN ties go to the even magnitude index; |v| > 6 saturates to 6;
+ *   - nibble = sign(v) << 3 | j, j = 3-bit magnitude index of
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}; packed codes: element 2m in the low nibble;
+ *   - dequantised value y = sign * fp32(fp32(val * s) * g), stored as bf16
+ *     (round to nearest even) or fp32.
+ *
+ * Guidance stream (a flat byte buffer, trace_guidance_bytes(n, k) long):
+ *   [ scale plane: n/16 E4M3 bytes | zero pad up to a multiple of 256 | bits ]
+ *   bits: element i's k bits at bit (i*k) mod 8 of byte floor(i*k/8) of the
+ *   bit plane, least significant first.  k = 1: the mantissa bit of the
+ *   rollout magnitude index; k = 2: its two low bits; k = 4: the whole nibble
+ *   (the bit plane then equals the packed code array).  The global scales
+ *   (f32[G]) travel beside the stream.
+ *
+ * Common rules for every entry point:
+ *   - pointers are device pointers unless stated; the caller owns every
+ *     buffer; the library never allocates device memory and keeps no state
+ *     beyond a read-only kernel table; calls are thread-safe;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns at once; outputs are valid once the stream has
+ *     reached that point;
+ *   - argument errors are found before anything is enqueued and returned as
+ *     a negative trace_status (nothing is written); TRACE_E_HIP reports a
+ *     failed launch; inputs must be finite (trace_amax can flag violations);
+ *   - n > 0, n % 16 == 0, n % (16 * G) == 0, n < 2^36, 1 <= G <= n / 16;
+ *   - every pointer 16-byte aligned; x / y_out may be the same buffer
+ *     (in-place fake-quant); any other overlap is undefined.
+ */
+#ifndef TRACE_QUANT_H
+#define TRACE_QUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRACE_OK = 0,
+    TRACE_E_NULL = -1,      /* a required pointer is NULL */
+    TRACE_E_SIZE = -2,      /* n or G violates the size rules */
+    TRACE_E_ALIGN = -3,     /* a pointer is not 16-byte aligned */
+    TRACE_E_K = -4,         /* unsupported guidance width */
+    TRACE_E_DTYPE = -5,     /* unknown output dtype */
+    TRACE_E_HIP = -6,       /* the HIP runtime reported an error */
+    TRACE_E_NONFINITE = -7  /* (device status word) an input was inf/NaN */
+} trace_status;
+
+typedef enum { TRACE_OUT_BF16 = 0, TRACE_OUT_F32 = 1 } trace_out_dtype;
+
+/* ---- sizes (host, pure; 0 for invalid arguments) --------------------- */
+
+/* Bytes of the packed code array: n / 2. */
+size_t trace_code_bytes(int64_t n);
+/* Bytes of the block-scale array: n / 16. */
+size_t trace_scale_bytes(int64_t n);
+/* Bytes of the guidance stream for width k in {1, 2, 4}:
+ * align256(n / 16) + n * k / 8. */
+size_t trace_guidance_bytes(int64_t n, int k);
+
+/* ---- rollout side ------------------------------------------------------ */
+
+/* Global scales.  "the same global scale" of the Figure 1 example.
+ * x_bf16: bf16[n].  g_out: f32[G], written with amax(|x| over group) / 2688.
+ * status_dev: nullable int*; if given and some input is inf or NaN,
+ * TRACE_E_NONFINITE is stored there (never cleared: the caller zeroes it).
+ * Enqueues three small kernels (clear, reduce, finalise). */
+int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_dev, void *stream);
+
+/* Rollout quantisation with standard RTN ("TRACE Core Concept": the rollout
+ * side's actual FP4 result), fused with the guidance emit.
+ * y_bf16: bf16[n]; g: f32[G] from trace_amax; k in {1, 2, 4}.
+ * codes: u8[n/2] packed nibbles; scales: u8[n/16] E4M3 block scales;
+ * guidance: u8[trace_guidance_bytes(n, k)] or NULL (no guidance written). */
+int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, int k,
+                        uint8_t *codes, uint8_t *scales, uint8_t *guidance, void *stream);
+
+/* Guidance stream from existing codes and scales (for example an FP4 KV cache
+ * written elsewhere); same layout as trace_quant_rollout's.  "TRACE Core
+ * Concept", compact-guidance paragraph.  codes: u8[n/2]; scales: u8[n/16];
+ * k in {1, 2, 4}; guidance: u8[trace_guidance_bytes(n, k)]. */
+int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, int k,
+                        uint8_t *guidance, void *stream);
+
+/* ---- training side ----------------------------------------------------- */
+
+/* Rollout-guided fake-quant ("TRACE Core Concept"): for each element, the
+ * two adjacent E2M1 points around v = x * inv (inv from the rollout's g and
+ * block scale); the rollout code is reconstructed as the code nearest v whose
+ * low k index bits equal the guidance bits; the adjacent point nearer it is
+ * chosen; ties fall back to RTN.
+ * x_bf16: bf16[n]; g: f32[G] (the rollout's); guidance: a k-bit stream;
+ * k in {1, 2}; y_out: bf16[n] or f32[n] per out_dtype; codes_out: nullable
+ * u8[n/2] receiving the chosen nibbles. */
+int trace_fakequant_guided(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *guidance,
+                           int k, void *y_out, int out_dtype, uint8_t *codes_out, void *stream);
+
+/* Full-code variant: the guidance carries the whole rollout nibble (k = 4
+ * stream), and the adjacent point nearer that code is chosen.  The costly
+ * option of "Experimental Results" (full guidance slows rollout). */
+int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *guidance,
+                             void *y_out, int out_dtype, uint8_t *codes_out, void *stream);
+
+/* Plain QAT fake-quant with RTN (the unstable baseline of "Experimental
+ * Results").  scales_in: NULL = compute block scales from x with g (then g
+ * should come from trace_amax on x); else u8[n/16] rollout scales (shared-
+ * scale RTN).  codes_out (u8[n/2]) and scales_out (u8[n/16]) are nullable. */
+int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales_in,
+                        void *y_out, int out_dtype, uint8_t *codes_out, uint8_t *scales_out, void *stream);
+
+/* ---- misc --------------------------------------------------------------- */
+
+/* Static string for a trace_status value. */
+const char *trace_status_str(int status);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int trace_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRACE_QUANT_H */

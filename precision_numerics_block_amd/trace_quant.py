@@ -1,0 +1,181 @@
+"""Thin ctypes binding of ``libtrace_quant.so`` (C ABI: include/trace_quant.h).
+
+Argument marshalling only: every function checks dtypes and devices, takes
+raw device pointers from torch tensors (``data_ptr()``) and the current HIP
+stream, and calls the C entry point of the same name.  torch supplies device
+memory and streams; every step of the computation runs in the library's HIP
+kernels.  Importing this module fails loudly when the library is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrace_quant.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "trace_code_bytes": (_sz, [_i64]),
+    "trace_scale_bytes": (_sz, [_i64]),
+    "trace_guidance_bytes": (_sz, [_i64, _int]),
+    "trace_amax": (_int, [_vp, _i64, _int, _vp, _vp, _vp]),
+    "trace_quant_rollout": (_int, [_vp, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp]),
+    "trace_guidance_pack": (_int, [_vp, _vp, _i64, _int, _vp, _vp]),
+    "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
+    "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
+    "trace_fakequant_rtn": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp]),
+    "trace_status_str": (ctypes.c_char_p, [_int]),
+    "trace_version": (_int, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+OUT_BF16, OUT_F32 = 0, 1
+
+__all__ = [
+    "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
+    "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
+]
+
+
+class TraceError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {lib.trace_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TraceError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _u8(n, dev):
+    return torch.empty(int(n), dtype=torch.uint8, device=dev)
+
+
+def code_bytes(n):
+    return int(lib.trace_code_bytes(int(n)))
+
+
+def scale_bytes(n):
+    return int(lib.trace_scale_bytes(int(n)))
+
+
+def guidance_bytes(n, k):
+    return int(lib.trace_guidance_bytes(int(n), int(k)))
+
+
+def version():
+    return int(lib.trace_version())
+
+
+def amax(x, G=1, out=None, status=None):
+    """Global scales f32[G] = amax(|x| per group) / 2688.  ``status``: optional
+    int32 GPU tensor of one element that receives TRACE_E_NONFINITE (-7)."""
+    _need(x, torch.bfloat16, "x")
+    g = torch.empty(G, dtype=torch.float32, device=x.device) if out is None else out
+    _check("trace_amax", lib.trace_amax(_ptr(x), x.numel(), int(G), _ptr(g), _ptr(status), _stream(x.device)))
+    return g
+
+
+def quant_rollout(y, g, k, G=1, guidance=True, codes=None, scales=None):
+    """RTN codes u8[n/2], E4M3 scales u8[n/16] and (if ``guidance``) the
+    guidance stream of width k.  ``guidance`` may be a preallocated tensor."""
+    _need(y, torch.bfloat16, "y")
+    _need(g, torch.float32, "g")
+    n, dev = y.numel(), y.device
+    codes = _u8(n // 2, dev) if codes is None else codes
+    scales = _u8(n // 16, dev) if scales is None else scales
+    if guidance is True:
+        guidance = _u8(guidance_bytes(n, k), dev)
+    elif guidance is False:
+        guidance = None
+    _check("trace_quant_rollout", lib.trace_quant_rollout(
+        _ptr(y), n, int(G), _ptr(g), int(k), _ptr(codes), _ptr(scales), _ptr(guidance), _stream(dev)))
+    return codes, scales, guidance
+
+
+def guidance_pack(codes, scales, n, k, out=None):
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    dev = codes.device
+    out = _u8(guidance_bytes(n, k), dev) if out is None else out
+    _check("trace_guidance_pack", lib.trace_guidance_pack(
+        _ptr(codes), _ptr(scales), int(n), int(k), _ptr(out), _stream(dev)))
+    return out
+
+
+def _outputs(x, out_dtype, out, codes_out):
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                          device=x.device)
+    if codes_out is True:
+        codes_out = _u8(x.numel() // 2, x.device)
+    elif codes_out is False:
+        codes_out = None
+    return out, codes_out
+
+
+def fakequant_guided(x, g, guidance, k, G=1, out_dtype=OUT_BF16, out=None, codes_out=None):
+    """Rollout-guided fake-quant; returns (y, codes_out or None)."""
+    _need(x, torch.bfloat16, "x")
+    _need(g, torch.float32, "g")
+    _need(guidance, torch.uint8, "guidance")
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    _check("trace_fakequant_guided", lib.trace_fakequant_guided(
+        _ptr(x), x.numel(), int(G), _ptr(g), _ptr(guidance), int(k), _ptr(out), int(out_dtype),
+        _ptr(codes_out), _stream(x.device)))
+    return out, codes_out
+
+
+def fakequant_fullcode(x, g, guidance, G=1, out_dtype=OUT_BF16, out=None, codes_out=None):
+    _need(x, torch.bfloat16, "x")
+    _need(g, torch.float32, "g")
+    _need(guidance, torch.uint8, "guidance")
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    _check("trace_fakequant_fullcode", lib.trace_fakequant_fullcode(
+        _ptr(x), x.numel(), int(G), _ptr(g), _ptr(guidance), _ptr(out), int(out_dtype),
+        _ptr(codes_out), _stream(x.device)))
+    return out, codes_out
+
+
+def fakequant_rtn(x, g, scales_in=None, G=1, out_dtype=OUT_BF16, out=None, codes_out=None, scales_out=None):
+    """Plain RTN fake-quant; own block scales when ``scales_in`` is None."""
+    _need(x, torch.bfloat16, "x")
+    _need(g, torch.float32, "g")
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    if scales_out is True:
+        scales_out = _u8(x.numel() // 16, x.device)
+    elif scales_out is False:
+        scales_out = None
+    _check("trace_fakequant_rtn", lib.trace_fakequant_rtn(
+        _ptr(x), x.numel(), int(G), _ptr(g), _ptr(scales_in), _ptr(out), int(out_dtype),
+        _ptr(codes_out), _ptr(scales_out), _stream(x.device)))
+    return out, codes_out, scales_out

@@ -1,0 +1,92 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/trace_quant.h declares, computes sizes on the host, and
+rejects bad arguments before it touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trace_quant.h")
+
+OK, E_NULL, E_SIZE, E_ALIGN, E_K, E_DTYPE = 0, -1, -2, -3, -4, -5
+A = 0x100000          # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def tq():
+    from precision_numerics_block_amd import trace_quant
+
+    return trace_quant
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(trace_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(tq):
+    names = declared_functions()
+    assert len(names) >= 11, names
+    for name in names:
+        assert hasattr(tq.lib, name), name
+    # and the binding wraps each of them
+    for name in names:
+        assert name in tq._SIGS
+
+
+def test_sizes(tq):
+    n = 16 * 40
+    assert tq.code_bytes(n) == n // 2
+    assert tq.scale_bytes(n) == n // 16
+    assert tq.guidance_bytes(n, 1) == 256 + n // 8
+    assert tq.guidance_bytes(n, 2) == 256 + n // 4
+    assert tq.guidance_bytes(n, 4) == 256 + n // 2
+    n = 16 * 256 * 3                         # scale plane exactly 768 bytes: no pad
+    assert tq.guidance_bytes(n, 2) == 768 + n // 4
+    assert tq.guidance_bytes(n, 3) == 0
+    assert tq.code_bytes(17) == 0 and tq.code_bytes(0) == 0
+    assert tq.version() >= 100
+    assert tq.lib.trace_status_str(-7).decode().startswith("an input")
+
+
+def test_argument_errors_before_any_hip_call(tq):
+    L = tq.lib
+    n = 16 * 64
+    # sizes
+    assert L.trace_amax(A, 0, 1, A, None, None) == E_SIZE
+    assert L.trace_amax(A, 24, 1, A, None, None) == E_SIZE
+    assert L.trace_amax(A, n, 3, A, None, None) == E_SIZE
+    assert L.trace_amax(A, n, 0, A, None, None) == E_SIZE
+    assert L.trace_amax(A, 1 << 36, 1, A, None, None) == E_SIZE
+    # null pointers
+    assert L.trace_amax(None, n, 1, A, None, None) == E_NULL
+    assert L.trace_quant_rollout(A, n, 1, None, 2, A, A, None, None) == E_NULL
+    assert L.trace_quant_rollout(A, n, 1, A, 2, None, A, None, None) == E_NULL
+    assert L.trace_guidance_pack(A, None, n, 2, A, None) == E_NULL
+    assert L.trace_fakequant_guided(A, n, 1, A, None, 2, A, 0, None, None) == E_NULL
+    assert L.trace_fakequant_fullcode(A, n, 1, A, None, A, 0, None, None) == E_NULL
+    assert L.trace_fakequant_rtn(A, n, 1, None, None, A, 0, None, None, None) == E_NULL
+    # alignment
+    assert L.trace_amax(A + 2, n, 1, A, None, None) == E_ALIGN
+    assert L.trace_quant_rollout(A, n, 1, A, 2, A + 8, A, None, None) == E_ALIGN
+    assert L.trace_fakequant_guided(A, n, 1, A, A + 1, 2, A, 0, None, None) == E_ALIGN
+    assert L.trace_fakequant_rtn(A, n, 1, A, A + 4, A, 0, None, None, None) == E_ALIGN
+    # guidance width and output dtype
+    assert L.trace_quant_rollout(A, n, 1, A, 3, A, A, A, None) == E_K
+    assert L.trace_guidance_pack(A, A, n, 0, A, None) == E_K
+    assert L.trace_fakequant_guided(A, n, 1, A, A, 4, A, 0, None, None) == E_K
+    assert L.trace_fakequant_guided(A, n, 1, A, A, 2, A, 7, None, None) == E_DTYPE
+    assert L.trace_fakequant_rtn(A, n, 1, A, None, A, 2, None, None, None) == E_DTYPE
+
+
+def test_binding_rejects_cpu_tensors(tq):
+    import torch
+
+    x = torch.zeros(64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tq.amax(x)
+    assert ctypes.sizeof(ctypes.c_void_p) == 8

@@ -1,0 +1,401 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: global scales, packed codes, block scales and guidance bytes bit-exact;
+bf16 fake-quant outputs bit-exact (bf16 has no slack below one rounding);
+fp32 fake-quant outputs within a relative 1e-6 (expected bit-exact, counted);
+chosen-code nibbles bit-exact.  Inputs come from the seeded generators or are
+constructed here; the oracle computes every expected value from those inputs
+alone (its own global scales, its own guidance), never from a GPU output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_numerics_block_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from precision_numerics_block_amd import trace_quant
+
+    return trace_quant
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield
+
+
+DEV = "cuda:0"
+
+
+def h16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+
+def h8(t):
+    return t.contiguous().cpu().numpy().reshape(-1)
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def assert_f32_close(got, want, what):
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    lim = REL_TOL * np.abs(want.astype(np.float64))
+    bad = err > lim
+    assert not bad.any(), f"{what}: {bad.sum()} outside rel {REL_TOL}, first at {np.argmax(bad)}"
+    assert np.array_equal(np.signbit(got), np.signbit(want)), f"{what}: sign bits differ"
+
+
+def assert_eq(got, want, what):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        idx = np.flatnonzero(got != want)
+        raise AssertionError(f"{what}: {idx.size} of {got.size} differ; first at {idx[0]}: "
+                             f"got {got[idx[0]]} want {want[idx[0]]}")
+
+
+def blocks_of(n_blocks, windows):
+    out = []
+    for b0, b1 in windows:
+        b0, b1 = max(0, b0), min(n_blocks, b1)
+        if b0 < b1:
+            out.append((b0, b1))
+    return out
+
+
+class Checker:
+    """Runs every entry point on the GPU once and compares chosen windows of
+    blocks (or everything) with the oracle."""
+
+    def __init__(self, tq, X, Y, k, G=1):
+        self.tq, self.X, self.Y, self.k, self.G = tq, X, Y, k, G
+        self.n = X.numel()
+        self.nblk = self.n // 16
+        self.Xh, self.Yh = h16(X), h16(Y)
+
+    def run_gpu(self, out_f32=False):
+        tq, X, Y, k, G = self.tq, self.X, self.Y, self.k, self.G
+        od = tq.OUT_F32 if out_f32 else tq.OUT_BF16
+        r = {}
+        st = torch.zeros(4, dtype=torch.int32, device=DEV)
+        r["gY"] = tq.amax(Y, G, status=st)
+        r["gX"] = tq.amax(X, G)
+        r["codes"], r["scales"], r["gd"] = tq.quant_rollout(Y, r["gY"], k, G)
+        r["pack"] = tq.guidance_pack(r["codes"], r["scales"], self.n, k)
+        if k in (1, 2):
+            r["yg"], r["cg"] = tq.fakequant_guided(X, r["gY"], r["gd"], k, G, od, codes_out=True)
+        else:
+            r["yg"], r["cg"] = tq.fakequant_fullcode(X, r["gY"], r["gd"], G, od, codes_out=True)
+        r["yr"], r["cr"], _ = tq.fakequant_rtn(X, r["gY"], r["scales"], G, od, codes_out=True)
+        r["yo"], r["co"], r["so"] = tq.fakequant_rtn(X, r["gX"], None, G, od, codes_out=True, scales_out=True)
+        torch.cuda.synchronize()
+        r["status"] = int(st[0].item())
+        self.r = r
+        self.out_f32 = out_f32
+        return r
+
+    def check(self, windows=None):
+        r, k, G, n = self.r, self.k, self.G, self.n
+        assert r["status"] == 0
+        gY, st = oracle.amax(self.Yh, G)
+        gX, _ = oracle.amax(self.Xh, G)
+        assert st == 0
+        assert_eq(r["gY"].cpu().numpy().view(np.uint32), gY.view(np.uint32), "global scales (rollout)")
+        assert_eq(r["gX"].cpu().numpy().view(np.uint32), gX.view(np.uint32), "global scales (training)")
+        full = windows is None
+        if full:
+            windows = [(0, self.nblk)]
+        codes = np.zeros(n // 2, np.uint8)
+        scales = np.zeros(n // 16, np.uint8)
+        gd = np.zeros(oracle.guidance_bytes(n, k), np.uint8)
+        off = oracle.bitplane_offset(n)
+        for b0, b1 in windows:
+            oracle.quant_rollout(self.Yh, gY, k, G, b0, b1, out=(codes, scales, gd))
+        for b0, b1 in windows:
+            e0, e1 = 16 * b0, 16 * b1
+            bk0, bk1 = off + b0 * 2 * k, off + b1 * 2 * k
+            assert_eq(h8(r["codes"][e0 // 2:e1 // 2]), codes[e0 // 2:e1 // 2], f"codes {b0}:{b1}")
+            assert_eq(h8(r["scales"][b0:b1]), scales[b0:b1], f"scales {b0}:{b1}")
+            assert_eq(h8(r["gd"][b0:b1]), gd[b0:b1], f"guidance scale plane {b0}:{b1}")
+            assert_eq(h8(r["gd"][bk0:bk1]), gd[bk0:bk1], f"guidance bits {b0}:{b1}")
+            assert_eq(h8(r["pack"][b0:b1]), gd[b0:b1], f"packed scale plane {b0}:{b1}")
+            assert_eq(h8(r["pack"][bk0:bk1]), gd[bk0:bk1], f"packed bits {b0}:{b1}")
+        if full:
+            assert_eq(h8(r["gd"]), gd, "whole guidance stream (with pad)")
+            assert_eq(h8(r["pack"]), gd, "whole packed stream (with pad)")
+        f32 = self.out_f32
+        for b0, b1 in windows:
+            e0, e1 = 16 * b0, 16 * b1
+            if k in (1, 2):
+                yg, cg = oracle.fakequant_guided(self.Xh, gY, gd, k, G, f32, b0, b1)
+            else:
+                yg, cg = oracle.fakequant_fullcode(self.Xh, gY, gd, G, f32, b0, b1)
+            yr, cr, _ = oracle.fakequant_rtn(self.Xh, gY, scales, G, f32, b0, b1)
+            yo, co, so = oracle.fakequant_rtn(self.Xh, gX, None, G, f32, b0, b1)
+            for name, got, want in (("guided", r["yg"], yg), ("rtn shared", r["yr"], yr),
+                                    ("rtn own", r["yo"], yo)):
+                g_ = got.reshape(-1)[e0:e1]
+                if f32:
+                    assert_f32_close(g_.cpu().numpy(), want[e0:e1], f"{name} y {b0}:{b1}")
+                else:
+                    assert_eq(h16(g_), want[e0:e1], f"{name} y {b0}:{b1}")
+            for name, got, want in (("guided", r["cg"], cg), ("rtn shared", r["cr"], cr),
+                                    ("rtn own", r["co"], co)):
+                assert_eq(h8(got[e0 // 2:e1 // 2]), want[e0 // 2:e1 // 2], f"{name} codes {b0}:{b1}")
+            assert_eq(h8(r["so"][b0:b1]), so[b0:b1], f"own scales {b0}:{b1}")
+
+
+# ---------------------------------------------------------------------------
+# Workloads at reduced row counts: the oracle checks every element
+# ---------------------------------------------------------------------------
+SMALL = [  # (workload, rows, tensor index)
+    (1, None, 0), (2, 2, 0), (3, 1024, 0), (3, 1024, 1), (4, 2048, 0), (4, 2048, 1), (5, 1, 0), (5, 1024, 2),
+]
+
+
+@pytest.mark.parametrize("wl,rows,ti", SMALL)
+def test_workload_small_full_parity(tq, wl, rows, ti):
+    name, shape = synth.tensor_specs(wl, rows)[ti]
+    X, Y = synth.make_pair(wl, ti, shape, DEV)
+    for k in synth.WORKLOADS[wl].ks + ((4,) if 4 not in synth.WORKLOADS[wl].ks else ()):
+        for G in (1, 4):
+            c = Checker(tq, X, Y, k, G)
+            c.run_gpu(out_f32=(k == 2 and G == 1))
+            c.check()
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, in the launch configuration the benchmark times: windows of
+# blocks (head, tail, the amax block, random) against the oracle
+# ---------------------------------------------------------------------------
+FULL = [(1, 0, 1), (2, 0, 1), (2, 0, 64), (3, 0, 1), (3, 1, 1), (4, 0, 1), (4, 1, 1), (5, 0, 1), (5, 1, 1),
+        (5, 2, 1)]
+
+
+@pytest.mark.parametrize("wl,ti,G", FULL)
+def test_workload_full_size_sampled(tq, wl, ti, G):
+    name, shape = synth.tensor_specs(wl)[ti]
+    X, Y = synth.make_pair(wl, ti, shape, DEV)
+    nblk = X.numel() // 16
+    rng = np.random.default_rng(wl * 100 + ti)
+    amax_blk = int(torch.argmax(Y.float().abs().reshape(-1)).item()) // 16
+    wins = [(0, 600), (nblk - 600, nblk), (amax_blk - 40, amax_blk + 40)]
+    for s in rng.integers(0, nblk - 300, 6):
+        wins.append((int(s), int(s) + 300))
+    wins = blocks_of(nblk, wins)
+    for k in synth.WORKLOADS[wl].ks:
+        c = Checker(tq, X, Y, k, G)
+        c.run_gpu(out_f32=False)
+        c.check(wins)
+    del X, Y
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Brute force over every finite bf16 value
+# ---------------------------------------------------------------------------
+def all_finite_bf16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = (b & 0x7F80) != 0x7F80
+    return b[fin]                                                  # 65280 values
+
+
+ANCHORS = [1e-38, 1.0, 6.0, 144.0, 2688.0, 3.0e37]
+
+
+def anchored_blocks():
+    """Every finite bf16 value, 15 per block after an anchor, for each anchor
+    (the anchor sets the block scale of most blocks)."""
+    vals = all_finite_bf16()
+    pad = (-vals.size) % 15
+    vals = np.concatenate([vals, vals[:pad]]).reshape(-1, 15)
+    out = []
+    for a in ANCHORS:
+        ab = torch.tensor([a], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        out.append(np.concatenate([np.full((vals.shape[0], 1), ab[0], np.uint16), vals], 1))
+    return np.concatenate(out).reshape(-1)
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_bruteforce_rollout_and_rtn(tq, k):
+    Yh = anchored_blocks()
+    nblk = Yh.size // 16
+    Y = to_dev_bf16(Yh)
+    # one global-scale group per block, so every anchor sets its own g
+    for G in (nblk, nblk // 8 if nblk % 8 == 0 else 1):
+        c = Checker(tq, Y, Y, k, G)
+        c.run_gpu(out_f32=False)
+        c.check()
+
+
+def synthetic_guidance(n, k, scale_bytes, gb_fn):
+    gd = np.zeros(oracle.guidance_bytes(n, k), np.uint8)
+    gd[: n // 16] = scale_bytes
+    off = oracle.bitplane_offset(n)
+    vals = gb_fn(np.arange(n)).astype(np.uint8)
+    bits = ((vals[:, None] >> np.arange(k)) & 1).astype(np.uint8).reshape(-1)
+    gd[off:] = np.packbits(bits, bitorder="little")
+    return gd
+
+
+# (g, E4M3 scale byte) pairs: powers of two (exact normalisation, so every
+# tie point is reached), an ordinary scale, subnormal scales, saturation.
+COMBOS = [(1.0, 0x38), (2.0 ** -10, 0x28), (1.0 / 2688.0, 0x7E), (3.7e-3, 0x5C), (1e-30, 0x01),
+          (1.0e20, 0x7E), (0.3, 0x00), (5.0e-3, 0x33)]
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_bruteforce_guided_all_bf16(tq, k, out_f32):
+    vals = all_finite_bf16()                                       # 4080 blocks
+    reps = 16 if k == 4 else (1 << k)
+    per = vals.size
+    Xh = np.tile(vals, len(COMBOS) * reps)
+    n = Xh.size
+    nblk = n // 16
+    blk_combo = (np.arange(nblk) // (per // 16)) // reps
+    blk_rep = (np.arange(nblk) // (per // 16)) % reps
+    g = np.array([COMBOS[c][0] for c in blk_combo], np.float32)
+    sb = np.array([COMBOS[c][1] for c in blk_combo], np.uint8)
+    gd = synthetic_guidance(n, k, sb, lambda i: blk_rep[i // 16])
+    X = to_dev_bf16(Xh)
+    gdev = torch.from_numpy(g).to(DEV)
+    gddev = torch.from_numpy(gd).to(DEV)
+    od = tq.OUT_F32 if out_f32 else tq.OUT_BF16
+    if k == 4:
+        y, c = tq.fakequant_fullcode(X, gdev, gddev, nblk, od, codes_out=True)
+        oy, oc = oracle.fakequant_fullcode(Xh, g, gd, nblk, out_f32)
+    else:
+        y, c = tq.fakequant_guided(X, gdev, gddev, k, nblk, od, codes_out=True)
+        oy, oc = oracle.fakequant_guided(Xh, g, gd, k, nblk, out_f32)
+    torch.cuda.synchronize()
+    assert_eq(h8(c), oc, f"chosen codes k={k}")
+    if out_f32:
+        assert_f32_close(y.cpu().numpy(), oy, f"y k={k}")
+    else:
+        assert_eq(h16(y), oy, f"y k={k}")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+def _pair_from_np(x, rel, seed):
+    rng = np.random.default_rng(seed)
+    X = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    xf = X.float().numpy()
+    y = xf + rel * np.abs(xf) * rng.standard_normal(xf.shape).astype(np.float32)
+    Y = torch.from_numpy(y).to(torch.bfloat16)
+    return X.to(DEV), Y.to(DEV)
+
+
+@pytest.mark.parametrize("nblk,G", [(1, 1), (2, 2), (37, 1), (512 + 37, 1), (3 * 512 + 6, 3),
+                                    (2048 * 512 + 1234, 1), (2048 * 513, 513)])
+def test_sizes_and_ragged_tails(tq, nblk, G):
+    rng = np.random.default_rng(nblk)
+    x = rng.standard_normal(16 * nblk) * np.exp(rng.uniform(-3, 3, 16 * nblk))
+    X, Y = _pair_from_np(x, 0.01, nblk)
+    for k in (1, 2, 4):
+        c = Checker(tq, X, Y, k, G)
+        c.run_gpu(out_f32=(k == 1))
+        if nblk > 100000:
+            c.check(blocks_of(nblk, [(0, 700), (nblk - 700, nblk), (nblk // 2, nblk // 2 + 700)]))
+        else:
+            c.check()
+
+
+@pytest.mark.parametrize("case", ["zeros", "negzeros", "tiny_amax", "huge", "mixed_tiny_blocks", "ties"])
+def test_degenerate_inputs(tq, case):
+    n = 16 * 1024
+    rng = np.random.default_rng(7)
+    if case == "zeros":
+        x = np.zeros(n)
+    elif case == "negzeros":
+        x = -np.zeros(n)
+    elif case == "tiny_amax":                        # g falls into fp32 subnormals
+        x = rng.standard_normal(n) * 1e-39
+    elif case == "huge":                             # near the bf16 maximum
+        x = rng.uniform(-2.5e38, 2.5e38, n)
+    elif case == "mixed_tiny_blocks":                # most block scales round to 0
+        x = rng.standard_normal(n) * 1e-6
+        x[::97] = 1e4
+    else:                                            # exact E2M1 ties at g = 1, s = 1
+        x = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 2.25, 4.5, 3.75], n) * rng.choice([-1, 1], n)
+        x[::16] = 6.0                                # block amax 6 -> t = 1 -> s = 1
+        x[0] = 2688.0                                # tensor amax -> g = 1
+    X, Y = _pair_from_np(x, 0.02, 11)
+    for k in (1, 2, 4):
+        c = Checker(tq, X, Y, k, 1)
+        c.run_gpu(out_f32=(k != 2))
+        c.check()
+
+
+def test_in_place_and_determinism(tq):
+    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
+    g = tq.amax(Y)
+    codes, scales, gd = tq.quant_rollout(Y, g, 2)
+    y1, c1 = tq.fakequant_guided(X, g, gd, 2, codes_out=True)
+    y2, c2 = tq.fakequant_guided(X, g, gd, 2, codes_out=True)
+    xin = X.clone()
+    y3, c3 = tq.fakequant_guided(xin, g, gd, 2, out=xin, codes_out=True)
+    codes2, scales2, gd2 = tq.quant_rollout(Y, g, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), xin.view(torch.int16))
+    assert torch.equal(c1, c2) and torch.equal(c1, c3)
+    assert torch.equal(codes, codes2) and torch.equal(gd, gd2) and torch.equal(scales, scales2)
+
+
+def test_guard_bytes_untouched(tq):
+    """Outputs carved out of larger buffers filled with a canary: nothing
+    outside the documented extents is written."""
+    n = 16 * (512 * 3 + 7)
+    X, Y = synth.make_pair(1, 0, (n // 2048 + 1, 2048), DEV)
+    X, Y = X.reshape(-1)[:n].contiguous(), Y.reshape(-1)[:n].contiguous()
+    pad = 4096
+    for k in (1, 2, 4):
+        gb = tq.guidance_bytes(n, k)
+        big_codes = torch.full((n // 2 + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+        big_scales = torch.full((n // 16 + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+        big_gd = torch.full((gb + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+        big_y = torch.full((n + 2 * pad,), 1.5, dtype=torch.bfloat16, device=DEV)
+        g = tq.amax(Y)
+        codes, scales, gd = big_codes[pad:pad + n // 2], big_scales[pad:pad + n // 16], big_gd[pad:pad + gb]
+        tq.quant_rollout(Y, g, k, 1, guidance=gd, codes=codes, scales=scales)
+        y = big_y[pad:pad + n]
+        if k == 4:
+            tq.fakequant_fullcode(X, g, gd, out=y)
+        else:
+            tq.fakequant_guided(X, g, gd, k, out=y)
+        torch.cuda.synchronize()
+        for big, m, fill in ((big_codes, n // 2, 0xA5), (big_scales, n // 16, 0xA5), (big_gd, gb, 0xA5)):
+            assert bool((big[:pad] == fill).all()) and bool((big[pad + m:] == fill).all())
+        assert bool((big_y[:pad] == 1.5).all()) and bool((big_y[pad + n:] == 1.5).all())
+
+
+def test_nonfinite_flag(tq):
+    x = np.ones(16 * 64, np.float32)
+    x[5] = np.inf
+    x[700] = np.nan
+    x[300] = 12.0
+    X = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    g = tq.amax(X, status=st)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -7
+    og, ost = oracle.amax(h16(X))
+    assert ost == -7
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
