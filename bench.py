@@ -1,0 +1,271 @@
+"""Benchmark of the rollout-guided FP4 fake-quant hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of routed-expert
+activations (64 experts x 512 tokens x 2048 hidden, bf16, Student-t(4),
+rollout copy with relative noise 0.01, k = 2 guidance bits):
+
+  rollout   amax(Y) -> RTN quantise + guidance (k = 2) -> full-code pack (k = 4)
+  training  guided fake-quant (k = 2) -> full-code fake-quant -> amax(X) ->
+            plain RTN fake-quant with own scales
+
+`value` is the whole step's algorithmic bytes per second (GB/s); `roofline`
+is the guided fake-quant kernel (the metric's subject) against the 8 TB/s
+HBM peak, timed with HIP events on the stream it runs on; `mismatch` holds
+the train/rollout code-mismatch rates; `cpu_baseline` is the CPU oracle on a
+bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+K_BITS = 2
+WORKLOAD = 2
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_expert_act_64x512x2048.txt")
+KERNEL_SRC = os.path.join(ROOT, "precision_numerics_block_amd", "csrc", "trace_quant.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-elems", type=int, default=1 << 23, help="oracle sample size (elements)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run a plain copy of this size (for counter calibration)")
+    return p.parse_args()
+
+
+def bytes_per_elem(k):
+    """Algorithmic bytes per element of each step kernel (read once, write once)."""
+    gbits = k / 8.0
+    return {
+        "amax_rollout": 2.0,
+        "quant_rollout": 2.0 + 0.5 + 1 / 16 + (1 / 16 + gbits),
+        "guidance_pack_full": (0.5 + 1 / 16) + (1 / 16 + 0.5),
+        "fakequant_guided": 2.0 + (1 / 16 + gbits) + 2.0,
+        "fakequant_fullcode": 2.0 + (1 / 16 + 0.5) + 2.0,
+        "amax_training": 2.0,
+        "fakequant_rtn_own": 2.0 + 2.0,
+    }
+
+
+def load_traffic():
+    """HBM bytes per launch of the guided kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    for line in open(PROFILE_TRAFFIC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(X, Y, n_sample):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    h = lambda t: t.reshape(-1)[:n_sample].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa
+    Xh, Yh = h(X), h(Y)
+    n = Xh.size
+    t0 = time.perf_counter()
+    g, _ = oracle.amax(Yh)
+    codes, scales, gd = oracle.quant_rollout(Yh, g, K_BITS)
+    gd4 = oracle.guidance_pack(codes, scales, n, 4)
+    oracle.fakequant_guided(Xh, g, gd, K_BITS, codes=False)
+    oracle.fakequant_fullcode(Xh, g, gd4, codes=False)
+    gx, _ = oracle.amax(Xh)
+    oracle.fakequant_rtn(Xh, gx, codes=False)
+    dt = time.perf_counter() - t0
+    step_bytes = sum(bytes_per_elem(K_BITS).values()) * n
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} elements ({n // (512 * 2048)} of 64 experts) of X and Y, whole step, "
+                      f"{dt:.1f} s single-threaded C"}
+
+
+def mismatch_stats(tq, X, Y, g, codes, scales, gd, gd4):
+    import torch
+
+    def signed(c):
+        c = c.to(torch.int32)
+        lo, hi = c & 15, c >> 4
+        nib = torch.stack([lo, hi], 1).reshape(-1)
+        mag = nib & 7
+        return torch.where((nib & 8) != 0, -mag, mag)
+
+    r = signed(codes)
+    _, c_rtn, _ = tq.fakequant_rtn(X, g, scales, codes_out=True)
+    _, c_gd = tq.fakequant_guided(X, g, gd, K_BITS, codes_out=True)
+    _, c_fc = tq.fakequant_fullcode(X, g, gd4, codes_out=True)
+    gx = tq.amax(X)
+    y_own, _, _ = tq.fakequant_rtn(X, gx)
+    y_roll, _, _ = tq.fakequant_rtn(Y, g, scales)       # the rollout's dequantised values
+    n = r.numel()
+    out = {}
+    for name, c in (("rtn_shared_scale", c_rtn), ("guided_k2", c_gd), ("full_code", c_fc)):
+        d = signed(c) - r
+        out[name] = round(float((d != 0).sum().item()) / n, 6)
+        if name == "rtn_shared_scale":
+            ad = d.abs()
+            hist = torch.bincount(ad[ad > 0], minlength=8)[1:8].tolist()
+            out["rtn_abs_index_step_hist"] = {str(i + 1): int(v) for i, v in enumerate(hist) if v}
+    own = (y_own.float() != y_roll.float()).sum().item()
+    out["rtn_own_scale_value"] = round(float(own) / n, 6)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the path has no multi-GPU leg: "
+              "each 16-element block is independent and shards need at most one max-reduction of the "
+              "global scale.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from precision_numerics_block_amd import synth, trace_quant as tq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name, shape = synth.tensor_specs(WORKLOAD)[0]
+    sets = [synth.make_pair(WORKLOAD, 0, shape, dev)]
+    # a second, differently seeded input set: consecutive steps alternate, so
+    # no step finds its inputs in the 256 MB last-level cache
+    X2 = sets[0][0].roll(1, 0).contiguous()
+    Y2 = sets[0][1].roll(1, 0).contiguous()
+    sets.append((X2, Y2))
+    n = sets[0][0].numel()
+    k = K_BITS
+    gbytes2 = tq.guidance_bytes(n, k)
+    gbytes4 = tq.guidance_bytes(n, 4)
+    bufs = []
+    for _ in sets:
+        bufs.append(dict(
+            g=torch.empty(1, dtype=torch.float32, device=dev),
+            gx=torch.empty(1, dtype=torch.float32, device=dev),
+            codes=torch.empty(n // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(n // 16, dtype=torch.uint8, device=dev),
+            gd=torch.empty(gbytes2, dtype=torch.uint8, device=dev),
+            gd4=torch.empty(gbytes4, dtype=torch.uint8, device=dev),
+            y_g=torch.empty(shape, dtype=torch.bfloat16, device=dev),
+            y_f=torch.empty(shape, dtype=torch.bfloat16, device=dev),
+            y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
+        ))
+    names = list(bytes_per_elem(k).keys())
+
+    def step(i, ev=None):
+        X, Y = sets[i % 2]
+        b = bufs[i % 2]
+        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        rec(0)
+        tq.amax(Y, out=b["g"])
+        rec(1)
+        tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+        rec(2)
+        tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
+        rec(3)
+        tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
+        rec(4)
+        tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
+        rec(5)
+        tq.amax(X, out=b["gx"])
+        rec(6)
+        tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
+        rec(7)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    per = {nm: 0.0 for nm in names}
+    for i in range(K):
+        for j, nm in enumerate(names):
+            per[nm] += evs[i][j].elapsed_time(evs[i][j + 1]) / K      # ms
+    bpe = bytes_per_elem(k)
+    step_bytes = sum(bpe.values()) * n
+    ms_step = (t1 - t0) * 1e3 / K
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    g_ms = per["fakequant_guided"]
+    g_bytes = bpe["fakequant_guided"] * n
+    achieved = g_bytes / (g_ms * 1e-3) / 1e9
+    kernels = {nm: {"us": round(per[nm] * 1e3, 2),
+                    "GBps": round(bpe[nm] * n / (per[nm] * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(bpe[nm] * n / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for nm in names}
+
+    if args.calib_copy_mib:
+        m = args.calib_copy_mib << 20
+        src = torch.empty(m, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    b = bufs[0]
+    X, Y = sets[0]
+    step(0)
+    mism = mismatch_stats(tq, X, Y, b["g"], b["codes"], b["scales"], b["gd"], b["gd4"])
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(X, Y, min(args.cpu_elems, n))
+
+    out = {
+        "metric": "guided FP4 fake-quant GB/s and % of HBM peak on 1 MI355X; mismatch rate",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "routed-expert activations 64x512x2048 bf16 (Student-t nu=4, rollout "
+                               "relative noise 0.01), k=2 guidance, G=1, whole rollout+training step",
+                   "elements": n, "k": k, "G": 1, "step_bytes": int(step_bytes)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
+                     "kernel": "k_fakequant<2,true,false> (trace_fakequant_guided, k=2, bf16 out)",
+                     "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "mismatch": mism,
+        "kernels": kernels,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

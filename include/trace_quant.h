@@ -48,7 +48,7 @@
  *   - argument errors are found before anything is enqueued and returned as
  *     a negative trace_status (nothing is written); TRACE_E_HIP reports a
  *     failed launch; inputs must be finite (trace_amax can flag violations);
- *   - n > 0, n % 16 == 0, n % (16 * G) == 0, n < 2^36, 1 <= G <= n / 16;
+ *   - n > 0, n % 16 == 0, n % (16 * G) == 0, n < 2^35, 1 <= G <= n / 16;
  *   - every pointer 16-byte aligned; x / y_out may be the same buffer
  *     (in-place fake-quant); any other overlap is undefined.
  */

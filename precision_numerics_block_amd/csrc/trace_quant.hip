@@ -11,18 +11,25 @@
 //
 // Design (one GPU, HBM-bound streaming; nothing here is a contraction, so no
 // MFMA):
-//   * one 16-element block per lane: each lane issues two 16-byte loads of
-//     bf16, so the block amax, the block scale and its reciprocal stay in the
-//     lane's registers (no cross-lane traffic at all);
+//   * one 8-element chunk per lane: a single 16-byte non-temporal load of bf16
+//     per lane, contiguous across the wavefront (a 16-byte-per-lane stream
+//     reaches ~6.1 TB/s on MI355X, 32 bytes per lane only ~5.5);
+//   * a 16-element block spans a lane pair: the block amax is a packed 16-bit
+//     max within the lane plus one DPP swap with the neighbour lane, so both
+//     lanes hold the block scale and its reciprocal in registers;
 //   * codes, scale bytes and guidance bits are packed in registers and
-//     written with one store per lane per plane (8, 1 and 2k bytes), which
-//     are contiguous across the wavefront;
-//   * the rounding decision of every mode is one fp32 compare against a
-//     threshold read from a 1.3 KB LDS table indexed by (mode row, bucket of
-//     |v|): chosen index = floor index + (|v| > threshold);
-//   * persistent workgroups walk tiles of 256 x kUnroll lane-blocks, loads
-//     of all kUnroll blocks first, so each wave keeps 32 x kUnroll bytes per
-//     lane in flight.
+//     written with one store per lane per plane (4, 1 and k bytes; scale
+//     bytes from the even lane), contiguous across the wavefront;
+//   * RTN to E2M1 uses gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1.0
+//     (two elements per instruction, nibbles packed in place) and the
+//     matching v_cvt_scalef32_pk_f32_fp4 to decode; bf16 outputs use
+//     v_cvt_pk_bf16_f32.  With scale 1.0 both conversions equal round to
+//     nearest even on every finite fp32 input (checked exhaustively);
+//   * the guided decision is one fp32 compare against a threshold read from
+//     a small LDS table indexed by (bucket of |v|, guidance value): chosen
+//     index = floor index + (|v| > threshold);
+//   * streaming kernels launch one tile of 256 x kUnroll chunks per
+//     workgroup (many small workgroups balance best across the 8 XCDs).
 #include <hip/hip_runtime.h>
 
 #include <bit>
@@ -33,30 +40,57 @@
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Launch shape and cache hints (fixed at build time; the values below are the
+// measured best on MI355X for the 64x512x2048 activation workload).
+#ifndef TRACE_UNROLL
+#define TRACE_UNROLL 2
+#endif
+#ifndef TRACE_WG_PER_CU
+#define TRACE_WG_PER_CU 0
+#endif
+#ifndef TRACE_NT_LOAD
+#define TRACE_NT_LOAD 1
+#endif
+#ifndef TRACE_NT_STORE
+#define TRACE_NT_STORE 0
+#endif
+
 constexpr int kThreads = 256;          // 4 wavefronts of 64
-constexpr int kUnroll = 2;             // lane-blocks per thread per tile
+constexpr int kUnroll = TRACE_UNROLL;  // chunks per thread per tile
 constexpr int kTile = kThreads * kUnroll;
-constexpr int kBuckets = 11;           // buckets of |v| (see bucket_of)
-constexpr int kMaxGrid = 256 * 8;      // 8 workgroups per CU
+constexpr int kMaxGrid = TRACE_WG_PER_CU > 0 ? 256 * TRACE_WG_PER_CU : 0x7fffffff;
+constexpr int kAmaxThreads = 1024;     // amax: one large workgroup per CU ...
+constexpr int kAmaxUnroll = 4;         // ... with 64 bytes in flight per lane
+constexpr int kAmaxTile = kAmaxThreads * kAmaxUnroll;
+constexpr int kAmaxGrid = 256;
+constexpr int kBuckets = 11;           // buckets of |v| (see decide)
+constexpr int kSlots = 16;             // table slots per row (bucket -> slot)
 
 // ---------------------------------------------------------------------------
-// Decision table.
+// Guided decision tables.
 //
 // |v| is split into 11 buckets by its fp32 exponent and top mantissa bit:
 //   [0,.25) [.25,.375) [.375,.5) [.5,.75) [.75,1) [1,1.5) [1.5,2) [2,3)
 //   [3,4) [4,6) [6,inf]
 // Within a bucket the floor E2M1 index jl is fixed (0 0 0 1 1 2 3 4 5 6 7)
-// and the upper neighbour is jl + 1.  For each (row, bucket) the table holds
+// and the upper neighbour is jl + 1.  For each (bucket, row) the table holds
 // a threshold T: the chosen index is jl + (|v| > T).  T >= value(jl), so an
 // on-grid |v| keeps jl; T = +inf always keeps jl; T = value(jl) always moves
 // up off the grid; a tie at x resolved upward is encoded as the float just
 // below x.  The second word holds bf16(value(jl + 1)) << 16 | bf16(value(jl)).
-//
-// Rows: 0 RTN; 1-2 guided k=1 (gb 0, 1); 3-6 guided k=2 (gb 0..3);
-//       7-14 full code (rollout magnitude index 0..7, sign checked apart).
+// Bucket f is found from c = clamp(|v|, 0.2, 6): bits(c) >> 22 runs over
+// 249 .. 259, and its low 4 bits, slot = (249 + f) & 15, are distinct, so the
+// table has 16 slots (slots 4 .. 8 unused) and the address needs no offset.
+// Layout: entry index = slot * rows + row; rows = 2 (k=1: gb), 4 (k=2: gb),
+// 8 (full code: rollout magnitude index, the sign is checked apart).
 // ---------------------------------------------------------------------------
-constexpr int kRowRtn = 0, kRowK1 = 1, kRowK2 = 3, kRowFull = 7, kRows = 15;
-
 constexpr float kGrid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 constexpr int kBucketFloor[kBuckets] = {0, 0, 0, 1, 1, 2, 3, 4, 5, 6, 7};
 
@@ -70,9 +104,6 @@ constexpr Rule L{'L', 0.0f, false};
 constexpr Rule H{'H', 0.0f, false};
 constexpr Rule Tlo(float x) { return Rule{'T', x, false}; }
 constexpr Rule Tup(float x) { return Rule{'T', x, true}; }
-
-// RTN: nearest, ties to the even index (midpoint of each bracket).
-constexpr Rule kRtn[7] = {Tlo(0.25f), Tup(0.75f), Tlo(1.25f), Tup(1.75f), Tlo(2.5f), Tup(3.5f), Tlo(5.0f)};
 
 // Guided, derived from the rule of "TRACE Core Concept" with the rollout
 // code reconstructed as the nearest code whose low k index bits equal gb:
@@ -114,30 +145,30 @@ constexpr Entry make_entry(Rule r, int jl)
     return Entry{thr, (hi << 16) | lo};
 }
 
+template <int R>
 struct Table {
-    Entry e[kRows * kBuckets];
+    Entry e[kSlots * R];
 };
 
-constexpr Table build_table()
+// mode: 1 = guided k=1, 2 = guided k=2, 4 = full code
+template <int MODE, int R>
+constexpr Table<R> build_table()
 {
-    Table t{};
+    Table<R> t{};
     for (int f = 0; f < kBuckets; ++f) {
         int jl = kBucketFloor[f];
         int b = jl < 7 ? jl : 0;
-        t.e[kRowRtn * kBuckets + f] = make_entry(kRtn[b], jl);
-        for (int gb = 0; gb < 2; ++gb)
-            t.e[(kRowK1 + gb) * kBuckets + f] = make_entry(kGuidedK1[b][gb], jl);
-        for (int gb = 0; gb < 4; ++gb)
-            t.e[(kRowK2 + gb) * kBuckets + f] = make_entry(kGuidedK2[b][gb], jl);
-        // full code: move up exactly when the rollout magnitude lies above jl
-        // (same sign is checked per element)
-        for (int r = 0; r < 8; ++r)
-            t.e[(kRowFull + r) * kBuckets + f] = make_entry(r > jl ? H : L, jl);
+        for (int r = 0; r < R; ++r) {
+            Rule rule = MODE == 1 ? kGuidedK1[b][r] : MODE == 2 ? kGuidedK2[b][r] : (r > jl ? H : L);
+            t.e[((249 + f) & 15) * R + r] = make_entry(rule, jl);
+        }
     }
     return t;
 }
 
-__constant__ Table kTable = build_table();
+__constant__ Table<2> kTabK1 = build_table<1, 2>();
+__constant__ Table<4> kTabK2 = build_table<2, 4>();
+__constant__ Table<8> kTabFull = build_table<4, 8>();
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -149,11 +180,11 @@ __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return as_f(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    uint32_t u = as_u(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // E4M3 (OCP "FN") encode of t >= 0: nearest, ties to even, saturating at 448,
@@ -194,17 +225,6 @@ __device__ __forceinline__ uint32_t block_scale(float ab, float g)
     return e4m3_encode(t);
 }
 
-__device__ __forceinline__ int bucket_of(uint32_t mag)
-{
-    int f = (int)(mag >> 22) - 249;
-    return min(max(f, 0), kBuckets - 1);
-}
-
-__device__ __forceinline__ uint32_t floor_index(int f)
-{
-    return f < 5 ? (uint32_t)(f >= 3) : (uint32_t)(f - 3);
-}
-
 // Unsigned division by an invariant d (Granlund & Montgomery 1994, Fig. 4.1).
 struct DivMagic {
     uint32_t m, s1, s2;
@@ -215,25 +235,62 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic d)
     return (t + ((n - t) >> d.s1)) >> d.s2;
 }
 
-struct Block16 {
-    uint32_t w[8];
-};
-
-__device__ __forceinline__ Block16 load_block(const uint4 *p, uint32_t lb)
+// Global scale of the group holding block blk (groups are bpg blocks long;
+// the index is clamped to the last group so a read can never leave g).
+template <bool kOneGroup>
+__device__ __forceinline__ float group_scale(const float *g, uint32_t blk, DivMagic dm, uint32_t last)
 {
-    uint4 a = p[2 * (size_t)lb];
-    uint4 b = p[2 * (size_t)lb + 1];
-    return Block16{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+    if (kOneGroup)
+        return g[0];
+    return g[min(div_magic(blk, dm), last)];
 }
 
-__device__ __forceinline__ float block_amax(const Block16 &x)
+template <class T>
+__device__ __forceinline__ T ld_stream(const T *p)
 {
-    uint32_t m = 0;
-    for (int i = 0; i < 8; ++i) {
-        uint32_t w = x.w[i] & 0x7fff7fffu;
-        m = max(m, max(w & 0xffffu, w >> 16));
-    }
-    return as_f(m << 16);
+#if TRACE_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <class T>
+__device__ __forceinline__ void st_stream(T v, T *p)
+{
+#if TRACE_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// 8 consecutive bf16 elements: element 2m is the low half of w[m].
+struct Chunk {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ Chunk load_chunk(const u32x4 *p, uint32_t c)
+{
+    u32x4 a = ld_stream(p + c);
+    return Chunk{{a.x, a.y, a.z, a.w}};
+}
+
+// max |x| over the chunk, as bf16 magnitude bits (finite inputs).
+__device__ __forceinline__ uint32_t chunk_amax_bits(const Chunk &x)
+{
+    u16x2 m = __builtin_bit_cast(u16x2, x.w[0] & 0x7fff7fffu);
+    for (int i = 1; i < 4; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x.w[i] & 0x7fff7fffu));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Combine with the neighbour lane (lane ^ 1) that holds the other half of the
+// block: DPP quad_perm [1,0,3,2].  Both lanes of a pair are always active
+// together (chunk counts are even and tiles start at even chunks).
+__device__ __forceinline__ uint32_t pair_max(uint32_t m)
+{
+    return max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xb1, 0xf, 0xf, false));
 }
 
 // k low bits of each of 8 nibbles of w, packed LSB-first (k = 1 or 2).
@@ -252,27 +309,61 @@ __device__ __forceinline__ uint32_t compact_k1(uint32_t w)
     return (x | (x >> 12)) & 0x000000ffu;
 }
 
-// Per-element decision: returns the chosen nibble and the dequantised value.
-// `row` selects the table row (already multiplied by kBuckets).
-__device__ __forceinline__ float decide(const Entry *tab, uint32_t row, float v, float s, float g, uint32_t &nib,
-                                        bool allow_up = true)
+// RTN of the 8 elements of a chunk times inv into 8 nibbles (element 2m low).
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest, ties to the
+// even E2M1 mantissa, saturates at +-6 and keeps the sign (also of -0).
+__device__ __forceinline__ uint32_t rtn8(const Chunk &x, float inv)
 {
-    uint32_t vb = as_u(v);
-    uint32_t mag = vb & 0x7fffffffu;
-    int f = bucket_of(mag);
-    Entry e = tab[row + f];
-    bool up = allow_up && (as_f(mag) > as_f(e.thr));
-    float val = as_f(up ? (e.vals & 0xffff0000u) : (e.vals << 16));
-    float y = (val * s) * g;
-    nib = (floor_index(f) + (up ? 1u : 0u)) | ((vb >> 28) & 8u);
-    return as_f(as_u(y) | (vb & 0x80000000u));
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf_lo(x.w[0]) * inv, bf_hi(x.w[0]) * inv, 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf_lo(x.w[1]) * inv, bf_hi(x.w[1]) * inv, 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf_lo(x.w[2]) * inv, bf_hi(x.w[2]) * inv, 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf_lo(x.w[3]) * inv, bf_hi(x.w[3]) * inv, 1.0f, 3);
+    return r;
 }
 
-__device__ __forceinline__ void load_table(Entry *lds, int rows_lo, int rows_hi)
+// Signed E2M1 values of the 8 nibbles of r (v_cvt_scalef32_pk_f32_fp4, scale 1).
+__device__ __forceinline__ void decode8(uint32_t r, float *out)
 {
-    for (int i = rows_lo * kBuckets + threadIdx.x; i < rows_hi * kBuckets; i += kThreads)
-        lds[i] = kTable.e[i];
-    __syncthreads();
+    f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 0);
+    f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 1);
+    f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 2);
+    f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 3);
+    out[0] = d0.x; out[1] = d0.y; out[2] = d1.x; out[3] = d1.y;
+    out[4] = d2.x; out[5] = d2.y; out[6] = d3.x; out[7] = d3.y;
+}
+
+// Floor E2M1 index of bucket f (0 0 0 1 1 2 3 4 5 6 7), from its slot.
+__device__ __forceinline__ uint32_t floor_index_of_slot(uint32_t slot)
+{
+    uint32_t f = (slot - 9u) & 15u;
+    return (f >= 3u ? 1u : 0u) + (f > 4u ? f - 4u : 0u);
+}
+
+// Bits of the chosen value: the high bf16 of `vals` when up, else the low
+// one, moved to the top half (v_perm_b32 byte select).
+__device__ __forceinline__ uint32_t pick_half(uint32_t vals, bool up)
+{
+    return __builtin_amdgcn_perm(0u, vals, up ? 0x03020c0cu : 0x01000c0cu);
+}
+
+// Guided / full-code decision for one element.  `row` is the guidance value
+// (gb, or the rollout magnitude index for full code); `allow` is false when
+// the full-code sign disagrees (then the point nearer zero is kept).
+template <int R, bool kCodes>
+__device__ __forceinline__ float decide(const Entry *tab, float v, uint32_t row, bool allow, float s, float g,
+                                        uint32_t &nib)
+{
+    float a = fabsf(v);
+    float c = __builtin_amdgcn_fmed3f(a, 0.2f, 6.0f);   // bucket clamp
+    uint32_t slot = (as_u(c) >> 22) & 15u;
+    Entry e = tab[slot * R + row];
+    bool up = allow && (a > as_f(e.thr));
+    float val = as_f(pick_half(e.vals, up));
+    float y = (val * s) * g;
+    if (kCodes)
+        nib = (floor_index_of_slot(slot) + (up ? 1u : 0u)) | ((as_u(v) >> 28) & 8u);
+    return as_f(as_u(y) | (as_u(v) & 0x80000000u));
 }
 
 struct OutPtr {
@@ -280,30 +371,45 @@ struct OutPtr {
     int f32;
 };
 
-__device__ __forceinline__ void store_y(OutPtr o, uint32_t lb, const float (&y)[16])
+__device__ __forceinline__ void store_y(OutPtr o, uint32_t c, const float (&y)[8])
 {
     if (o.f32) {
-        float4 *p = reinterpret_cast<float4 *>(o.y) + 4 * (size_t)lb;
-        for (int q = 0; q < 4; ++q)
-            p[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+        f32x4 *p = reinterpret_cast<f32x4 *>(o.y) + 2 * (size_t)c;
+        st_stream(f32x4{y[0], y[1], y[2], y[3]}, p);
+        st_stream(f32x4{y[4], y[5], y[6], y[7]}, p + 1);
     } else {
-        uint32_t w[8];
-        for (int i = 0; i < 8; ++i)
-            w[i] = f32_to_bf16(y[2 * i]) | (f32_to_bf16(y[2 * i + 1]) << 16);
-        uint4 *p = reinterpret_cast<uint4 *>(o.y) + 2 * (size_t)lb;
-        p[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        p[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        u32x4 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+        st_stream(w, reinterpret_cast<u32x4 *>(o.y) + c);
     }
 }
 
-// Global scale of the group holding lane-block lb (groups are bpg blocks
-// long; the index is clamped to the last group so a read can never leave g).
-template <bool kOneGroup>
-__device__ __forceinline__ float group_scale(const float *g, uint32_t lb, DivMagic dm, uint32_t last)
+template <int R>
+__device__ __forceinline__ void load_table(Entry *lds, const Entry *src)
 {
-    if (kOneGroup)
-        return g[0];
-    return g[min(div_magic(lb, dm), last)];
+    for (int i = threadIdx.x; i < kSlots * R; i += kThreads)
+        lds[i] = src[i];
+    __syncthreads();
+}
+
+// Zero the pad between the scale plane and the bit plane of a guidance stream.
+__device__ __forceinline__ void zero_pad(uint8_t *gd, uint32_t begin, uint32_t end)
+{
+    if (blockIdx.x == 0)
+        for (uint32_t p = begin + threadIdx.x; p < end; p += kThreads)
+            gd[p] = 0;
+}
+
+// Guidance bits of one chunk (8 codes in cw): k = 1 -> 1 byte, 2 -> 2 bytes,
+// 4 -> the 4 code bytes.
+template <int K>
+__device__ __forceinline__ void store_bits(uint8_t *gd_bits, uint32_t c, uint32_t cw)
+{
+    if (K == 4)
+        reinterpret_cast<uint32_t *>(gd_bits)[c] = cw;
+    else if (K == 2)
+        reinterpret_cast<uint16_t *>(gd_bits)[c] = (uint16_t)compact_k2(cw);
+    else
+        gd_bits[c] = (uint8_t)compact_k1(cw);
 }
 
 // ---------------------------------------------------------------------------
@@ -317,57 +423,75 @@ __global__ void k_amax_clear(uint32_t *g_bits, int G)
         g_bits[i] = 0u;
 }
 
-__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+// Fold the workgroup's running max and raise the group's word with one atomic
+// max, skipped when the word already holds a value at least as large.
+__device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint32_t *word)
 {
+    uint32_t m = run;
     for (int off = 32; off > 0; off >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    return v;
+        m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if ((threadIdx.x & 63) == 0)
+        wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = 0;
+        for (int i = 0; i < kAmaxThreads / 64; ++i)
+            b = max(b, wmax[i]);
+        b <<= 16;
+        if (b > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(word, b);
+    }
+    __syncthreads();
 }
 
-// Group amax as float bits (|bf16| << 16 orders like the float), atomicMax
-// per wave on each group change.  Work items are (group, tile) pairs; each
-// workgroup takes a contiguous range of items.
-__global__ void __launch_bounds__(kThreads) k_amax(const uint4 *__restrict__ x, uint32_t bpg, uint32_t tiles_per_group,
-                                                  uint64_t items, uint32_t *g_bits, int *status)
+// Group amax as float bits (|bf16| << 16 orders like the float).  Work items
+// are (group, tile) pairs walked grid-stride; each thread keeps a running max
+// for the current group and the workgroup publishes it when the group changes
+// and at the end.  Non-finite inputs are left out and flagged.
+__global__ void __launch_bounds__(kAmaxThreads)
+    k_amax(const u32x4 *__restrict__ x, uint32_t cpg, uint32_t tiles_per_group, uint32_t items,
+           uint32_t *g_bits, int *status)
 {
-    uint64_t per_wg = (items + gridDim.x - 1) / gridDim.x;
-    uint64_t w0 = (uint64_t)blockIdx.x * per_wg;
-    uint64_t w1 = min(items, w0 + per_wg);
-    uint32_t run = 0, bad = 0;
-    int64_t cur = -1;
-    for (uint64_t w = w0; w < w1; ++w) {
-        uint32_t grp = (uint32_t)(w / tiles_per_group);
-        uint32_t tile = (uint32_t)(w - (uint64_t)grp * tiles_per_group);
-        if ((int64_t)grp != cur) {
-            if (cur >= 0) {
-                uint32_t m = wave_max(run);
-                if ((threadIdx.x & 63) == 0 && m)
-                    atomicMax(g_bits + cur, m);
+    __shared__ uint32_t wmax[kAmaxThreads / 64];
+    uint32_t run = 0;
+    uint32_t cur = 0xffffffffu;
+    for (uint32_t w = blockIdx.x; w < items; w += gridDim.x) {
+        uint32_t grp = w / tiles_per_group;
+        uint32_t tile = w - grp * tiles_per_group;
+        if (grp != cur) {
+            if (cur != 0xffffffffu) {
+                amax_publish(run, wmax, g_bits + cur);
+                run = 0;
             }
             cur = grp;
-            run = 0;
         }
-        uint32_t base = grp * bpg;
-        for (int u = 0; u < kUnroll; ++u) {
-            uint32_t j = tile * kTile + u * kThreads + threadIdx.x;
-            if (j < bpg) {
-                Block16 b = load_block(x, base + j);
-                for (int i = 0; i < 8; ++i) {
-                    uint32_t lo = b.w[i] & 0x7fffu, hi = (b.w[i] >> 16) & 0x7fffu;
-                    bool flo = lo < 0x7f80u, fhi = hi < 0x7f80u;
-                    bad |= (!flo) | (!fhi);
-                    run = max(run, max(flo ? lo << 16 : 0u, fhi ? hi << 16 : 0u));
+        uint32_t base = grp * cpg;
+        Chunk b[kAmaxUnroll];
+        bool ok[kAmaxUnroll];
+        for (int u = 0; u < kAmaxUnroll; ++u) {
+            uint32_t j = tile * kAmaxTile + u * kAmaxThreads + threadIdx.x;
+            ok[u] = j < cpg;
+            if (ok[u])
+                b[u] = load_chunk(x, base + j);
+        }
+        for (int u = 0; u < kAmaxUnroll; ++u) {
+            if (!ok[u])
+                continue;
+            uint32_t m = chunk_amax_bits(b[u]);
+            if (m >= 0x7f80u) {                            // rare: an inf or NaN in the chunk
+                m = 0;
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t lo = b[u].w[i] & 0x7fffu, hi = (b[u].w[i] >> 16) & 0x7fffu;
+                    m = max(m, max(lo < 0x7f80u ? lo : 0u, hi < 0x7f80u ? hi : 0u));
                 }
+                if (status)
+                    *status = TRACE_E_NONFINITE;
             }
+            run = max(run, m);
         }
     }
-    if (cur >= 0) {
-        uint32_t m = wave_max(run);
-        if ((threadIdx.x & 63) == 0 && m)
-            atomicMax(g_bits + cur, m);
-    }
-    if (bad && status)
-        *status = TRACE_E_NONFINITE;
+    if (cur != 0xffffffffu)
+        amax_publish(run, wmax, g_bits + cur);
 }
 
 __global__ void k_amax_finalize(float *g, int G)
@@ -380,52 +504,40 @@ __global__ void k_amax_finalize(float *g, int G)
 // Rollout: RTN codes, scale bytes, and (optionally) the guidance stream.
 template <int K, bool kOneGroup>
 __global__ void __launch_bounds__(kThreads)
-    k_quant_rollout(const uint4 *__restrict__ y, uint32_t nblk, const float *__restrict__ g, DivMagic dm,
-                    uint32_t last_group,
-                    uint2 *__restrict__ codes, uint8_t *__restrict__ scales, uint8_t *__restrict__ gd_scales,
-                    uint8_t *__restrict__ gd_bits, uint32_t pad_begin, uint32_t pad_end)
+    k_quant_rollout(const u32x4 *__restrict__ y, uint32_t nchunk, const float *__restrict__ g, DivMagic dm,
+                    uint32_t last_group, uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                    uint8_t *__restrict__ gd_scales, uint8_t *__restrict__ gd_bits, uint32_t pad_begin,
+                    uint32_t pad_end)
 {
-    __shared__ Entry tab[kRows * kBuckets];
-    load_table(tab, kRowRtn, kRowRtn + 1);
-    if (gd_scales && blockIdx.x == 0)
-        for (uint32_t p = pad_begin + threadIdx.x; p < pad_end; p += kThreads)
-            gd_scales[p] = 0;
-    uint32_t ntiles = (nblk + kTile - 1) / kTile;
+    if (gd_scales)
+        zero_pad(gd_scales, pad_begin, pad_end);
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        Block16 xb[kUnroll];
-        uint32_t lbs[kUnroll];
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll];
         for (int u = 0; u < kUnroll; ++u) {
-            lbs[u] = t * kTile + u * kThreads + threadIdx.x;
-            if (lbs[u] < nblk)
-                xb[u] = load_block(y, lbs[u]);
+            cs[u] = t * kTile + u * kThreads + threadIdx.x;
+            if (cs[u] < nchunk)
+                xc[u] = load_chunk(y, cs[u]);
         }
         for (int u = 0; u < kUnroll; ++u) {
-            uint32_t lb = lbs[u];
-            if (lb >= nblk)
+            uint32_t c = cs[u];
+            if (c >= nchunk)
                 continue;
-            float gg = group_scale<kOneGroup>(g, lb, dm, last_group);
-            uint32_t sc = block_scale(block_amax(xb[u]), gg);
-            float s = e4m3_decode(sc);
-            float inv = inv_combined(s, gg);
-            uint32_t nw[2] = {0u, 0u};
-            for (int i = 0; i < 16; ++i) {
-                uint32_t w = xb[u].w[i >> 1];
-                float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * inv;
-                uint32_t nib;
-                decide(tab, kRowRtn * kBuckets, v, s, gg, nib);
-                nw[i >> 3] |= nib << (4 * (i & 7));
+            uint32_t blk = c >> 1;
+            float gg = group_scale<kOneGroup>(g, blk, dm, last_group);
+            uint32_t ab = pair_max(chunk_amax_bits(xc[u]));
+            uint32_t sc = block_scale(as_f(ab << 16), gg);
+            float inv = inv_combined(e4m3_decode(sc), gg);
+            uint32_t cw = rtn8(xc[u], inv);
+            st_stream(cw, codes + c);
+            if ((c & 1u) == 0) {
+                scales[blk] = (uint8_t)sc;
+                if (gd_scales)
+                    gd_scales[blk] = (uint8_t)sc;
             }
-            codes[lb] = make_uint2(nw[0], nw[1]);
-            scales[lb] = (uint8_t)sc;
-            if (gd_scales) {
-                gd_scales[lb] = (uint8_t)sc;
-                if (K == 4)
-                    reinterpret_cast<uint2 *>(gd_bits)[lb] = make_uint2(nw[0], nw[1]);
-                else if (K == 2)
-                    reinterpret_cast<uint32_t *>(gd_bits)[lb] = compact_k2(nw[0]) | (compact_k2(nw[1]) << 16);
-                else
-                    reinterpret_cast<uint16_t *>(gd_bits)[lb] = (uint16_t)(compact_k1(nw[0]) | (compact_k1(nw[1]) << 8));
-            }
+            if (gd_scales)
+                store_bits<K>(gd_bits, c, cw);
         }
     }
 }
@@ -433,92 +545,120 @@ __global__ void __launch_bounds__(kThreads)
 // Guidance stream from codes + scales.
 template <int K>
 __global__ void __launch_bounds__(kThreads)
-    k_guidance_pack(const uint2 *__restrict__ codes, const uint8_t *__restrict__ scales, uint32_t nblk,
+    k_guidance_pack(const uint32_t *__restrict__ codes, const uint8_t *__restrict__ scales, uint32_t nchunk,
                     uint8_t *__restrict__ gd_scales, uint8_t *__restrict__ gd_bits, uint32_t pad_begin,
                     uint32_t pad_end)
 {
-    if (blockIdx.x == 0)
-        for (uint32_t p = pad_begin + threadIdx.x; p < pad_end; p += kThreads)
-            gd_scales[p] = 0;
-    for (uint32_t lb = blockIdx.x * kThreads + threadIdx.x; lb < nblk; lb += gridDim.x * kThreads) {
-        uint2 c = codes[lb];
-        gd_scales[lb] = scales[lb];
-        if (K == 4)
-            reinterpret_cast<uint2 *>(gd_bits)[lb] = c;
-        else if (K == 2)
-            reinterpret_cast<uint32_t *>(gd_bits)[lb] = compact_k2(c.x) | (compact_k2(c.y) << 16);
-        else
-            reinterpret_cast<uint16_t *>(gd_bits)[lb] = (uint16_t)(compact_k1(c.x) | (compact_k1(c.y) << 8));
+    zero_pad(gd_scales, pad_begin, pad_end);
+    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunk; c += gridDim.x * kThreads) {
+        uint32_t cw = ld_stream(codes + c);
+        if ((c & 1u) == 0)
+            gd_scales[c >> 1] = scales[c >> 1];
+        store_bits<K>(gd_bits, c, cw);
     }
 }
 
-// Training side.  MODE: 1, 2 = guided with k bits; 4 = full code;
-// 0 = RTN with shared scales (from the scale plane / scales_in);
-// 5 = RTN with own scales computed from x.
+// Training side, guided (MODE 1, 2: k guidance bits) or full code (MODE 4).
 template <int MODE, bool kOneGroup, bool kCodes>
 __global__ void __launch_bounds__(kThreads)
-    k_fakequant(const uint4 *x, uint32_t nblk, const float *__restrict__ g, DivMagic dm, uint32_t last_group,
-                const uint8_t *__restrict__ scale_plane, const uint8_t *__restrict__ bits, OutPtr out,
-                uint2 *__restrict__ codes_out, uint8_t *__restrict__ scales_out)
+    k_fakequant_guided(const u32x4 *x, uint32_t nchunk, const float *__restrict__ g, DivMagic dm,
+                       uint32_t last_group, const uint8_t *__restrict__ scale_plane,
+                       const uint8_t *__restrict__ bits, OutPtr out, uint32_t *__restrict__ codes_out)
 {
-    __shared__ Entry tab[kRows * kBuckets];
-    constexpr int lo = MODE == 1 ? kRowK1 : MODE == 2 ? kRowK2 : MODE == 4 ? kRowFull : kRowRtn;
-    constexpr int hi = MODE == 1 ? kRowK1 + 2 : MODE == 2 ? kRowK2 + 4 : MODE == 4 ? kRowFull + 8 : kRowRtn + 1;
-    load_table(tab, lo, hi);
-    uint32_t ntiles = (nblk + kTile - 1) / kTile;
+    constexpr int R = MODE == 1 ? 2 : MODE == 2 ? 4 : 8;
+    __shared__ Entry tab[kSlots * R];
+    load_table<R>(tab, MODE == 1 ? kTabK1.e : MODE == 2 ? kTabK2.e : kTabFull.e);
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        Block16 xb[kUnroll];
-        uint32_t lbs[kUnroll], sc[kUnroll];
-        uint2 gb[kUnroll];
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll], sc[kUnroll], gb[kUnroll];
         for (int u = 0; u < kUnroll; ++u) {
-            uint32_t lb = t * kTile + u * kThreads + threadIdx.x;
-            lbs[u] = lb;
-            if (lb < nblk) {
-                xb[u] = load_block(x, lb);
-                if (MODE != 5)
-                    sc[u] = scale_plane[lb];
+            uint32_t c = t * kTile + u * kThreads + threadIdx.x;
+            cs[u] = c;
+            if (c < nchunk) {
+                xc[u] = load_chunk(x, c);
+                sc[u] = scale_plane[c >> 1];
                 if (MODE == 1)
-                    gb[u] = make_uint2(reinterpret_cast<const uint16_t *>(bits)[lb], 0u);
+                    gb[u] = bits[c];
                 else if (MODE == 2)
-                    gb[u] = make_uint2(reinterpret_cast<const uint32_t *>(bits)[lb], 0u);
-                else if (MODE == 4)
-                    gb[u] = reinterpret_cast<const uint2 *>(bits)[lb];
+                    gb[u] = reinterpret_cast<const uint16_t *>(bits)[c];
+                else
+                    gb[u] = ld_stream(reinterpret_cast<const uint32_t *>(bits) + c);
             }
         }
         for (int u = 0; u < kUnroll; ++u) {
-            uint32_t lb = lbs[u];
-            if (lb >= nblk)
+            uint32_t c = cs[u];
+            if (c >= nchunk)
                 continue;
-            float gg = group_scale<kOneGroup>(g, lb, dm, last_group);
-            uint32_t s8 = MODE == 5 ? block_scale(block_amax(xb[u]), gg) : (sc[u] & 0x7fu);
-            float s = e4m3_decode(s8);
+            float gg = group_scale<kOneGroup>(g, c >> 1, dm, last_group);
+            float s = e4m3_decode(sc[u] & 0x7fu);
             float inv = inv_combined(s, gg);
-            float yv[16];
-            uint32_t nw[2] = {0u, 0u};
-            for (int i = 0; i < 16; ++i) {
-                uint32_t w = xb[u].w[i >> 1];
+            float yv[8];
+            uint32_t nw = 0;
+            for (int i = 0; i < 8; ++i) {
+                uint32_t w = xc[u].w[i >> 1];
                 float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * inv;
-                uint32_t row, nib;
+                uint32_t row, nib = 0;
                 bool allow = true;
                 if (MODE == 1) {
-                    row = (kRowK1 + ((gb[u].x >> i) & 1u)) * kBuckets;
+                    row = (gb[u] >> i) & 1u;
                 } else if (MODE == 2) {
-                    row = (kRowK2 + ((gb[u].x >> (2 * i)) & 3u)) * kBuckets;
-                } else if (MODE == 4) {
-                    uint32_t r = ((i < 8 ? gb[u].x : gb[u].y) >> (4 * (i & 7))) & 0xfu;
-                    row = (kRowFull + (r & 7u)) * kBuckets;
-                    allow = ((r >> 3) == (as_u(v) >> 31));
+                    row = (gb[u] >> (2 * i)) & 3u;
                 } else {
-                    row = kRowRtn * kBuckets;
+                    uint32_t r = (gb[u] >> (4 * i)) & 0xfu;
+                    row = r & 7u;
+                    allow = (r >> 3) == (as_u(v) >> 31);
                 }
-                yv[i] = decide(tab, row, v, s, gg, nib, allow);
-                nw[i >> 3] |= nib << (4 * (i & 7));
+                yv[i] = decide<R, kCodes>(tab, v, row, allow, s, gg, nib);
+                if (kCodes)
+                    nw |= nib << (4 * i);
             }
-            store_y(out, lb, yv);
+            store_y(out, c, yv);
             if (kCodes)
-                codes_out[lb] = make_uint2(nw[0], nw[1]);
-            if (MODE == 5 && scales_out)
-                scales_out[lb] = (uint8_t)s8;
+                st_stream(nw, codes_out + c);
+        }
+    }
+}
+
+// Training side, plain RTN: shared scales from `scales_in` (kOwn = false) or
+// block scales computed from x (kOwn = true, optionally written out).
+template <bool kOwn, bool kOneGroup, bool kCodes>
+__global__ void __launch_bounds__(kThreads)
+    k_fakequant_rtn(const u32x4 *x, uint32_t nchunk, const float *__restrict__ g, DivMagic dm, uint32_t last_group,
+                    const uint8_t *__restrict__ scales_in, OutPtr out, uint32_t *__restrict__ codes_out,
+                    uint8_t *__restrict__ scales_out)
+{
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll], sc[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = t * kTile + u * kThreads + threadIdx.x;
+            cs[u] = c;
+            if (c < nchunk) {
+                xc[u] = load_chunk(x, c);
+                if (!kOwn)
+                    sc[u] = scales_in[c >> 1];
+            }
+        }
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = cs[u];
+            if (c >= nchunk)
+                continue;
+            float gg = group_scale<kOneGroup>(g, c >> 1, dm, last_group);
+            uint32_t s8 = kOwn ? block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg) : (sc[u] & 0x7fu);
+            float s = e4m3_decode(s8);
+            float inv = inv_combined(s, gg);
+            uint32_t cw = rtn8(xc[u], inv);
+            float yv[8];
+            decode8(cw, yv);
+            for (int i = 0; i < 8; ++i)
+                yv[i] = (yv[i] * s) * gg;               // signed value: the sign rides along
+            store_y(out, c, yv);
+            if (kCodes)
+                st_stream(cw, codes_out + c);
+            if (kOwn && scales_out && (c & 1u) == 0)
+                scales_out[c >> 1] = (uint8_t)s8;
         }
     }
 }
@@ -526,7 +666,7 @@ __global__ void __launch_bounds__(kThreads)
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int64_t kMaxN = int64_t(1) << 36;
+constexpr int64_t kMaxN = int64_t(1) << 35;   // chunk indices (n / 8) fit in 32 bits
 
 DivMagic make_div_magic(uint32_t d)
 {
@@ -548,47 +688,68 @@ int check_sizes(int64_t n, int G)
     return TRACE_OK;
 }
 
-int grid_for(uint32_t nblk)
+int grid_for(uint32_t nchunk)
 {
-    uint32_t tiles = (nblk + kTile - 1) / kTile;
+    uint32_t tiles = (nchunk + kTile - 1) / kTile;
     return (int)(tiles < (uint32_t)kMaxGrid ? tiles : (uint32_t)kMaxGrid);
 }
 
-int launched()
-{
-    return hipGetLastError() == hipSuccess ? TRACE_OK : TRACE_E_HIP;
-}
+int launched() { return hipGetLastError() == hipSuccess ? TRACE_OK : TRACE_E_HIP; }
 
 int64_t bitplane_offset(int64_t n) { return (n / 16 + 255) / 256 * 256; }
 
-template <int MODE, bool kOneGroup>
-void launch_fq(dim3 grid, hipStream_t st, const uint4 *x, uint32_t nblk, const float *g, DivMagic dm,
-               uint32_t last, const uint8_t *sp, const uint8_t *bits, OutPtr out, uint2 *codes, uint8_t *scales_out)
+struct Launch {
+    dim3 grid;
+    hipStream_t st;
+    uint32_t nchunk;
+    DivMagic dm;
+    uint32_t last;
+    bool one;
+};
+
+Launch plan(int64_t n, int G, void *stream)
 {
-    if (codes)
-        hipLaunchKernelGGL((k_fakequant<MODE, kOneGroup, true>), grid, dim3(kThreads), 0, st, x, nblk, g, dm, last,
-                           sp, bits, out, codes, scales_out);
-    else
-        hipLaunchKernelGGL((k_fakequant<MODE, kOneGroup, false>), grid, dim3(kThreads), 0, st, x, nblk, g, dm, last,
-                           sp, bits, out, codes, scales_out);
+    uint32_t nchunk = (uint32_t)(n / 8);
+    uint32_t nblk = (uint32_t)(n / 16);
+    return Launch{dim3(grid_for(nchunk)), (hipStream_t)stream, nchunk, make_div_magic(nblk / (uint32_t)G),
+                  (uint32_t)G - 1u, G == 1};
 }
 
 template <int MODE>
-int fakequant_any(const void *x, int64_t n, int G, const float *g, const uint8_t *sp, const uint8_t *bits, void *y,
-                  int out_dtype, uint8_t *codes, uint8_t *scales_out, void *stream)
+int launch_guided(const Launch &L, const void *x, const float *g, const uint8_t *sp, const uint8_t *bits,
+                  OutPtr out, uint8_t *codes)
 {
-    uint32_t nblk = (uint32_t)(n / 16);
-    DivMagic dm = make_div_magic(nblk / (uint32_t)G);
-    dim3 grid(grid_for(nblk));
-    hipStream_t st = (hipStream_t)stream;
-    OutPtr out{y, out_dtype == TRACE_OUT_F32};
     (void)hipGetLastError();
-    if (G == 1)
-        launch_fq<MODE, true>(grid, st, (const uint4 *)x, nblk, g, dm, 0u, sp, bits, out, (uint2 *)codes,
-                              scales_out);
-    else
-        launch_fq<MODE, false>(grid, st, (const uint4 *)x, nblk, g, dm, (uint32_t)G - 1u, sp, bits, out,
-                               (uint2 *)codes, scales_out);
+    const u32x4 *xp = (const u32x4 *)x;
+    uint32_t *cp = (uint32_t *)codes;
+#define TRACE_G(ONE, CODES)                                                                                    \
+    hipLaunchKernelGGL((k_fakequant_guided<MODE, ONE, CODES>), L.grid, dim3(kThreads), 0, L.st, xp, L.nchunk, g, \
+                       L.dm, L.last, sp, bits, out, cp)
+    if (L.one) {
+        if (codes) TRACE_G(true, true); else TRACE_G(true, false);
+    } else {
+        if (codes) TRACE_G(false, true); else TRACE_G(false, false);
+    }
+#undef TRACE_G
+    return launched();
+}
+
+template <bool kOwn>
+int launch_rtn(const Launch &L, const void *x, const float *g, const uint8_t *scales_in, OutPtr out, uint8_t *codes,
+               uint8_t *scales_out)
+{
+    (void)hipGetLastError();
+    const u32x4 *xp = (const u32x4 *)x;
+    uint32_t *cp = (uint32_t *)codes;
+#define TRACE_R(ONE, CODES)                                                                                   \
+    hipLaunchKernelGGL((k_fakequant_rtn<kOwn, ONE, CODES>), L.grid, dim3(kThreads), 0, L.st, xp, L.nchunk, g, \
+                       L.dm, L.last, scales_in, out, cp, scales_out)
+    if (L.one) {
+        if (codes) TRACE_R(true, true); else TRACE_R(true, false);
+    } else {
+        if (codes) TRACE_R(false, true); else TRACE_R(false, false);
+    }
+#undef TRACE_R
     return launched();
 }
 
@@ -631,14 +792,14 @@ int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_d
     if (!aligned16(x_bf16) || !aligned16(g_out) || (status_dev && !aligned16(status_dev)))
         return TRACE_E_ALIGN;
     hipStream_t st = (hipStream_t)stream;
-    uint32_t nblk = (uint32_t)(n / 16), bpg = nblk / (uint32_t)G;
-    uint32_t tpg = (bpg + kTile - 1) / kTile;
-    uint64_t items = (uint64_t)tpg * (uint64_t)G;
-    int grid = (int)(items < (uint64_t)kMaxGrid ? items : (uint64_t)kMaxGrid);
+    uint32_t nchunk = (uint32_t)(n / 8), cpg = nchunk / (uint32_t)G;
+    uint32_t tpg = (cpg + kAmaxTile - 1) / kAmaxTile;
+    uint64_t items = (uint64_t)tpg * (uint64_t)G;         // <= nchunk < 2^32
+    int grid = (int)(items < (uint64_t)kAmaxGrid ? items : (uint64_t)kAmaxGrid);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_amax_clear, dim3((G + 255) / 256), dim3(256), 0, st, (uint32_t *)g_out, G);
-    hipLaunchKernelGGL(k_amax, dim3(grid), dim3(kThreads), 0, st, (const uint4 *)x_bf16, bpg, tpg, items,
-                       (uint32_t *)g_out, status_dev);
+    hipLaunchKernelGGL(k_amax, dim3(grid), dim3(kAmaxThreads), 0, st, (const u32x4 *)x_bf16, cpg, tpg,
+                       (uint32_t)items, (uint32_t *)g_out, status_dev);
     hipLaunchKernelGGL(k_amax_finalize, dim3((G + 255) / 256), dim3(256), 0, st, g_out, G);
     return launched();
 }
@@ -656,26 +817,23 @@ int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, in
         return TRACE_E_ALIGN;
     if (k != 1 && k != 2 && k != 4)
         return TRACE_E_K;
-    uint32_t nblk = (uint32_t)(n / 16);
-    DivMagic dm = make_div_magic(nblk / (uint32_t)G);
-    dim3 grid(grid_for(nblk));
-    hipStream_t st = (hipStream_t)stream;
+    Launch L = plan(n, G, stream);
     uint8_t *bits = guidance ? guidance + bitplane_offset(n) : nullptr;
-    uint32_t pb = nblk, pe = (uint32_t)bitplane_offset(n);
+    uint32_t pb = (uint32_t)(n / 16), pe = (uint32_t)bitplane_offset(n);
     (void)hipGetLastError();
-#define TRACE_LAUNCH_ROLLOUT(KK, ONE)                                                                            \
-    hipLaunchKernelGGL((k_quant_rollout<KK, ONE>), grid, dim3(kThreads), 0, st, (const uint4 *)y_bf16, nblk, g, dm, \
-                       (uint32_t)G - 1u, (uint2 *)codes, scales, guidance, bits, pb, pe)
-    if (G == 1) {
-        if (k == 1) TRACE_LAUNCH_ROLLOUT(1, true);
-        else if (k == 2) TRACE_LAUNCH_ROLLOUT(2, true);
-        else TRACE_LAUNCH_ROLLOUT(4, true);
+#define TRACE_Q(KK, ONE)                                                                                            \
+    hipLaunchKernelGGL((k_quant_rollout<KK, ONE>), L.grid, dim3(kThreads), 0, L.st, (const u32x4 *)y_bf16, L.nchunk, \
+                       g, L.dm, L.last, (uint32_t *)codes, scales, guidance, bits, pb, pe)
+    if (L.one) {
+        if (k == 1) TRACE_Q(1, true);
+        else if (k == 2) TRACE_Q(2, true);
+        else TRACE_Q(4, true);
     } else {
-        if (k == 1) TRACE_LAUNCH_ROLLOUT(1, false);
-        else if (k == 2) TRACE_LAUNCH_ROLLOUT(2, false);
-        else TRACE_LAUNCH_ROLLOUT(4, false);
+        if (k == 1) TRACE_Q(1, false);
+        else if (k == 2) TRACE_Q(2, false);
+        else TRACE_Q(4, false);
     }
-#undef TRACE_LAUNCH_ROLLOUT
+#undef TRACE_Q
     return launched();
 }
 
@@ -690,22 +848,23 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
         return TRACE_E_ALIGN;
     if (k != 1 && k != 2 && k != 4)
         return TRACE_E_K;
-    uint32_t nblk = (uint32_t)(n / 16);
-    uint32_t wgs = (nblk + kThreads - 1) / kThreads;
+    uint32_t nchunk = (uint32_t)(n / 8);
+    uint32_t wgs = (nchunk + kThreads - 1) / kThreads;
     dim3 grid(wgs < (uint32_t)kMaxGrid ? wgs : (uint32_t)kMaxGrid);
     hipStream_t st = (hipStream_t)stream;
     uint8_t *bits = guidance + bitplane_offset(n);
-    uint32_t pb = nblk, pe = (uint32_t)bitplane_offset(n);
+    uint32_t pb = (uint32_t)(n / 16), pe = (uint32_t)bitplane_offset(n);
+    const uint32_t *cp = (const uint32_t *)codes;
     (void)hipGetLastError();
     if (k == 1)
-        hipLaunchKernelGGL((k_guidance_pack<1>), grid, dim3(kThreads), 0, st, (const uint2 *)codes, scales, nblk,
-                           guidance, bits, pb, pe);
+        hipLaunchKernelGGL((k_guidance_pack<1>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
+                           pe);
     else if (k == 2)
-        hipLaunchKernelGGL((k_guidance_pack<2>), grid, dim3(kThreads), 0, st, (const uint2 *)codes, scales, nblk,
-                           guidance, bits, pb, pe);
+        hipLaunchKernelGGL((k_guidance_pack<2>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
+                           pe);
     else
-        hipLaunchKernelGGL((k_guidance_pack<4>), grid, dim3(kThreads), 0, st, (const uint2 *)codes, scales, nblk,
-                           guidance, bits, pb, pe);
+        hipLaunchKernelGGL((k_guidance_pack<4>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
+                           pe);
     return launched();
 }
 
@@ -721,10 +880,12 @@ int trace_fakequant_guided(const void *x_bf16, int64_t n, int G, const float *g,
         return TRACE_E_ALIGN;
     if (k != 1 && k != 2)
         return TRACE_E_K;
+    Launch L = plan(n, G, stream);
+    OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
     const uint8_t *bits = guidance + bitplane_offset(n);
     if (k == 1)
-        return fakequant_any<1>(x_bf16, n, G, g, guidance, bits, y_out, out_dtype, codes_out, nullptr, stream);
-    return fakequant_any<2>(x_bf16, n, G, g, guidance, bits, y_out, out_dtype, codes_out, nullptr, stream);
+        return launch_guided<1>(L, x_bf16, g, guidance, bits, out, codes_out);
+    return launch_guided<2>(L, x_bf16, g, guidance, bits, out, codes_out);
 }
 
 int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *guidance,
@@ -737,8 +898,9 @@ int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *
         return TRACE_E_NULL;
     if (!aligned16(guidance) || (codes_out && !aligned16(codes_out)))
         return TRACE_E_ALIGN;
-    const uint8_t *bits = guidance + bitplane_offset(n);
-    return fakequant_any<4>(x_bf16, n, G, g, guidance, bits, y_out, out_dtype, codes_out, nullptr, stream);
+    Launch L = plan(n, G, stream);
+    OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
+    return launch_guided<4>(L, x_bf16, g, guidance, guidance + bitplane_offset(n), out, codes_out);
 }
 
 int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales_in, void *y_out,
@@ -750,16 +912,17 @@ int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, co
     if ((scales_in && !aligned16(scales_in)) || (codes_out && !aligned16(codes_out)) ||
         (scales_out && !aligned16(scales_out)))
         return TRACE_E_ALIGN;
+    Launch L = plan(n, G, stream);
+    OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
     if (scales_in) {
-        rc = fakequant_any<0>(x_bf16, n, G, g, scales_in, nullptr, y_out, out_dtype, codes_out, nullptr, stream);
+        rc = launch_rtn<false>(L, x_bf16, g, scales_in, out, codes_out, nullptr);
         if (rc == TRACE_OK && scales_out)
-            rc = hipMemcpyAsync(scales_out, scales_in, (size_t)(n / 16), hipMemcpyDeviceToDevice,
-                                (hipStream_t)stream) == hipSuccess
+            rc = hipMemcpyAsync(scales_out, scales_in, (size_t)(n / 16), hipMemcpyDeviceToDevice, L.st) == hipSuccess
                      ? TRACE_OK
                      : TRACE_E_HIP;
         return rc;
     }
-    return fakequant_any<5>(x_bf16, n, G, g, nullptr, nullptr, y_out, out_dtype, codes_out, scales_out, stream);
+    return launch_rtn<true>(L, x_bf16, g, nullptr, out, codes_out, scales_out);
 }
 
 const char *trace_status_str(int status)
@@ -767,7 +930,7 @@ const char *trace_status_str(int status)
     switch (status) {
     case TRACE_OK: return "ok";
     case TRACE_E_NULL: return "a required pointer is NULL";
-    case TRACE_E_SIZE: return "n or G violates the size rules (n > 0, n % 16 == 0, n % (16 G) == 0, n < 2^36)";
+    case TRACE_E_SIZE: return "n or G violates the size rules (n > 0, n % 16 == 0, n % (16 G) == 0, n < 2^35)";
     case TRACE_E_ALIGN: return "a pointer is not 16-byte aligned";
     case TRACE_E_K: return "unsupported guidance width k";
     case TRACE_E_DTYPE: return "unknown output dtype";
@@ -777,6 +940,6 @@ const char *trace_status_str(int status)
     }
 }
 
-int trace_version(void) { return 100; }
+int trace_version(void) { return 300; }
 
 }  // extern "C"
