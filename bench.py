@@ -8,11 +8,12 @@ rollout copy with relative noise 0.01, k = 2 guidance bits):
   training  guided fake-quant (k = 2) -> full-code fake-quant -> amax(X) ->
             plain RTN fake-quant with own scales
 
-`value` is the whole step's algorithmic bytes per second (GB/s); `roofline`
-is the guided fake-quant kernel (the metric's subject) against the 8 TB/s
-HBM peak, timed with HIP events on the stream it runs on; `mismatch` holds
-the train/rollout code-mismatch rates; `cpu_baseline` is the CPU oracle on a
-bounded sample of the same step.
+`value` is the whole step's algorithmic bytes per second (GB/s) over K timed
+steps; `roofline` is the guided fake-quant kernel (the metric's subject)
+against the 8 TB/s HBM peak, its launch duration timed with HIP events on the
+stream it runs on over K back-to-back launches; `kernels` gives the same for
+every step kernel; `mismatch` holds the train/rollout code-mismatch rates;
+`cpu_baseline` is the CPU oracle on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu]
 """
@@ -39,7 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--cpu-elems", type=int, default=1 << 23, help="oracle sample size (elements)")
+    p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
+    p.add_argument("--cpu-elems", type=int, default=1 << 25, help="oracle sample size (elements)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain copy of this size (for counter calibration)")
     return p.parse_args()
@@ -172,46 +174,90 @@ def main():
         ))
     names = list(bytes_per_elem(k).keys())
 
-    def step(i, ev=None):
+    def launch(nm, i):
+        """One launch of step kernel `nm` on input set i % 2."""
         X, Y = sets[i % 2]
         b = bufs[i % 2]
-        rec = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
-        rec(0)
-        tq.amax(Y, out=b["g"])
-        rec(1)
-        tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
-        rec(2)
-        tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
-        rec(3)
-        tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
-        rec(4)
-        tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
-        rec(5)
-        tq.amax(X, out=b["gx"])
-        rec(6)
-        tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
-        rec(7)
+        if nm == "amax_rollout":
+            tq.amax(Y, out=b["g"])
+        elif nm == "quant_rollout":
+            tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+        elif nm == "guidance_pack_full":
+            tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
+        elif nm == "fakequant_guided":
+            tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
+        elif nm == "fakequant_fullcode":
+            tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
+        elif nm == "amax_training":
+            tq.amax(X, out=b["gx"])
+        else:
+            tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
+
+    def step(i):
+        for nm in names:
+            launch(nm, i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    # The step is captured once per input set into a HIP graph (11 kernel
+    # launches, no memset/memcpy nodes) and replayed; eager launching is
+    # timed too, for reference.
+    graphs = []
+    if not args.eager:
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            for i in range(2):
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph, stream=s_cap):
+                    step(i)
+                graphs.append(gph)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        for i in range(2 * args.warmup):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
 
-    per = {nm: 0.0 for nm in names}
-    for i in range(K):
-        for j, nm in enumerate(names):
-            per[nm] += evs[i][j].elapsed_time(evs[i][j + 1]) / K      # ms
+    def run_steps(K, use_graph):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(K):
+            if use_graph:
+                graphs[i % 2].replay()
+            else:
+                step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / K, e0.elapsed_time(e1) / K
+
+    # timed region 1: K whole steps (the headline value)
+    K = args.steps
+    ms_eager, gpu_ms_eager = run_steps(K, False)
+    if graphs:
+        ms_step, gpu_ms_step = run_steps(K, True)
+    else:
+        ms_step, gpu_ms_step = ms_eager, gpu_ms_eager
+
+    # timed region 2: per-kernel launch durations, K back-to-back launches of
+    # each kernel on alternating input sets, HIP events on the launch stream
+    # (a single launch between two events would also count the event's own
+    # dispatch and release, ~2-4 us)
+    per = {}
+    for nm in names:
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(K):
+            launch(nm, i)
+        b_.record()
+        torch.cuda.synchronize()
+        per[nm] = a.elapsed_time(b_) / K                   # ms per launch
+
     bpe = bytes_per_elem(k)
     step_bytes = sum(bpe.values()) * n
-    ms_step = (t1 - t0) * 1e3 / K
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
     g_ms = per["fakequant_guided"]
@@ -248,6 +294,9 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "gpu_ms_per_step": round(gpu_ms_step, 4),
+        "launch": "hip graph replay" if graphs else "eager",
+        "ms_per_step_eager": round(ms_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -258,7 +307,7 @@ def main():
                    "elements": n, "k": k, "G": 1, "step_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
-                     "kernel": "k_fakequant<2,true,false> (trace_fakequant_guided, k=2, bf16 out)",
+                     "kernel": "k_fakequant_guided<2,true,false> (trace_fakequant_guided, k=2, bf16 out)",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "mismatch": mism,

@@ -850,7 +850,8 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
         return TRACE_E_K;
     uint32_t nchunk = (uint32_t)(n / 8);
     uint32_t wgs = (nchunk + kThreads - 1) / kThreads;
-    dim3 grid(wgs < (uint32_t)kMaxGrid ? wgs : (uint32_t)kMaxGrid);
+    const uint32_t pack_grid = 256 * 8;                  // persistent: 8 workgroups per CU
+    dim3 grid(wgs < pack_grid ? wgs : pack_grid);
     hipStream_t st = (hipStream_t)stream;
     uint8_t *bits = guidance + bitplane_offset(n);
     uint32_t pb = (uint32_t)(n / 16), pe = (uint32_t)bitplane_offset(n);

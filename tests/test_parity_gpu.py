@@ -399,3 +399,46 @@ def test_nonfinite_flag(tq):
     og, ost = oracle.amax(h16(X))
     assert ost == -7
     assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+
+
+def test_graph_replay_matches_eager(tq):
+    """The whole step captured into a HIP graph: every replay (with eager work
+    and synchronisation between replays) reproduces the eager outputs."""
+    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
+    n = X.numel()
+    g, gx = torch.empty(1, device=DEV), torch.empty(1, device=DEV)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=DEV)
+    gd = torch.empty(tq.guidance_bytes(n, 2), dtype=torch.uint8, device=DEV)
+    gd4 = torch.empty(tq.guidance_bytes(n, 4), dtype=torch.uint8, device=DEV)
+    yg, yf, yr = (torch.empty_like(X) for _ in range(3))
+
+    def step():
+        tq.amax(Y, out=g)
+        tq.quant_rollout(Y, g, 2, guidance=gd, codes=codes, scales=scales)
+        tq.guidance_pack(codes, scales, n, 4, out=gd4)
+        tq.fakequant_guided(X, g, gd, 2, out=yg)
+        tq.fakequant_fullcode(X, g, gd4, out=yf)
+        tq.amax(X, out=gx)
+        tq.fakequant_rtn(X, gx, out=yr)
+
+    outs = (g, gx, codes, scales, gd, gd4, yg, yf, yr)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.view(torch.uint8).fill_(0xA5 if rep % 2 else 0x00)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
