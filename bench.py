@@ -1,21 +1,23 @@
 """Benchmark of the rollout-guided FP4 fake-quant hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of routed-expert
-activations (64 experts x 512 tokens x 2048 hidden, bf16, Student-t(4),
-rollout copy with relative noise 0.01, k = 2 guidance bits):
+One step = one pass of the whole path over one batch of a workload.  For each
+tensor of the workload (default: routed-expert activations 64 experts x 512
+tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
+0.01, k = 2 guidance bits):
 
-  rollout   amax(Y) -> RTN quantise + guidance (k = 2) -> full-code pack (k = 4)
-  training  guided fake-quant (k = 2) -> full-code fake-quant -> amax(X) ->
+  rollout   amax(Y) -> RTN quantise + guidance (k) -> full-code pack (k = 4)
+  training  guided fake-quant (k) -> full-code fake-quant -> amax(X) ->
             plain RTN fake-quant with own scales
 
 `value` is the whole step's algorithmic bytes per second (GB/s) over K timed
-steps; `roofline` is the guided fake-quant kernel (the metric's subject)
-against the 8 TB/s HBM peak, its launch duration timed with HIP events on the
-stream it runs on over K back-to-back launches; `kernels` gives the same for
-every step kernel; `mismatch` holds the train/rollout code-mismatch rates;
-`cpu_baseline` is the CPU oracle on a bounded sample of the same step.
+steps, replayed from a HIP graph; `roofline` is the guided fake-quant kernel
+(the metric's subject) against the 8 TB/s HBM peak, its launch duration timed
+with HIP events on the stream it runs on over K back-to-back launches;
+`kernels` gives the same for every step kernel; `mismatch` holds the
+train/rollout code-mismatch rates; `cpu_baseline` is the CPU oracle on a
+bounded sample of the same step.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--k 1|2] [--no-cpu]
 """
 import argparse
 import hashlib
@@ -28,10 +30,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-K_BITS = 2
-WORKLOAD = 2
+DEFAULT_WORKLOAD = 2
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_expert_act_64x512x2048.txt")
 KERNEL_SRC = os.path.join(ROOT, "precision_numerics_block_amd", "csrc", "trace_quant.hip")
+
+KERNELS = ["amax_rollout", "quant_rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode",
+           "amax_training", "fakequant_rtn_own"]
 
 
 def parse():
@@ -39,6 +43,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--k", type=int, default=2, choices=[1, 2], help="guidance bits of the compact stream")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
     p.add_argument("--cpu-elems", type=int, default=1 << 25, help="oracle sample size (elements)")
@@ -80,7 +86,7 @@ def load_traffic():
         return None
 
 
-def cpu_baseline(X, Y, n_sample):
+def cpu_baseline(X, Y, n_sample, k):
     import numpy as np
     import torch
 
@@ -91,20 +97,22 @@ def cpu_baseline(X, Y, n_sample):
     n = Xh.size
     t0 = time.perf_counter()
     g, _ = oracle.amax(Yh)
-    codes, scales, gd = oracle.quant_rollout(Yh, g, K_BITS)
+    codes, scales, gd = oracle.quant_rollout(Yh, g, k)
     gd4 = oracle.guidance_pack(codes, scales, n, 4)
-    oracle.fakequant_guided(Xh, g, gd, K_BITS, codes=False)
+    oracle.fakequant_guided(Xh, g, gd, k, codes=False)
     oracle.fakequant_fullcode(Xh, g, gd4, codes=False)
     gx, _ = oracle.amax(Xh)
     oracle.fakequant_rtn(Xh, gx, codes=False)
     dt = time.perf_counter() - t0
-    step_bytes = sum(bytes_per_elem(K_BITS).values()) * n
+    step_bytes = sum(bytes_per_elem(k).values()) * n
     return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements ({n // (512 * 2048)} of 64 experts) of X and Y, whole step, "
-                      f"{dt:.1f} s single-threaded C"}
+            "sample": f"first {n} elements of the first tensor's X and Y, whole step, {dt:.1f} s "
+                      f"single-threaded C"}
 
 
-def mismatch_stats(tq, X, Y, g, codes, scales, gd, gd4):
+def mismatch_stats(tq, pairs, bufs, k):
+    """Element-level code mismatch between the training side and the rollout
+    codes, summed over the workload's tensors."""
     import torch
 
     def signed(c):
@@ -114,24 +122,26 @@ def mismatch_stats(tq, X, Y, g, codes, scales, gd, gd4):
         mag = nib & 7
         return torch.where((nib & 8) != 0, -mag, mag)
 
-    r = signed(codes)
-    _, c_rtn, _ = tq.fakequant_rtn(X, g, scales, codes_out=True)
-    _, c_gd = tq.fakequant_guided(X, g, gd, K_BITS, codes_out=True)
-    _, c_fc = tq.fakequant_fullcode(X, g, gd4, codes_out=True)
-    gx = tq.amax(X)
-    y_own, _, _ = tq.fakequant_rtn(X, gx)
-    y_roll, _, _ = tq.fakequant_rtn(Y, g, scales)       # the rollout's dequantised values
-    n = r.numel()
-    out = {}
-    for name, c in (("rtn_shared_scale", c_rtn), ("guided_k2", c_gd), ("full_code", c_fc)):
-        d = signed(c) - r
-        out[name] = round(float((d != 0).sum().item()) / n, 6)
-        if name == "rtn_shared_scale":
-            ad = d.abs()
-            hist = torch.bincount(ad[ad > 0], minlength=8)[1:8].tolist()
-            out["rtn_abs_index_step_hist"] = {str(i + 1): int(v) for i, v in enumerate(hist) if v}
-    own = (y_own.float() != y_roll.float()).sum().item()
-    out["rtn_own_scale_value"] = round(float(own) / n, 6)
+    tot = {"rtn_shared_scale": 0, "guided": 0, "full_code": 0, "rtn_own_scale_value": 0}
+    hist = torch.zeros(8, dtype=torch.int64, device=pairs[0][0].device)
+    n_all = 0
+    for (X, Y), b in zip(pairs, bufs):
+        r = signed(b["codes"])
+        _, c_rtn, _ = tq.fakequant_rtn(X, b["g"], b["scales"], codes_out=True)
+        _, c_gd = tq.fakequant_guided(X, b["g"], b["gd"], k, codes_out=True)
+        _, c_fc = tq.fakequant_fullcode(X, b["g"], b["gd4"], codes_out=True)
+        y_own, _, _ = tq.fakequant_rtn(X, b["gx"])
+        y_roll, _, _ = tq.fakequant_rtn(Y, b["g"], b["scales"])   # the rollout's dequantised values
+        for name, c in (("rtn_shared_scale", c_rtn), ("guided", c_gd), ("full_code", c_fc)):
+            d = signed(c) - r
+            tot[name] += int((d != 0).sum().item())
+            if name == "rtn_shared_scale":
+                ad = d.abs()
+                hist += torch.bincount(ad[ad > 0], minlength=8)[:8]
+        tot["rtn_own_scale_value"] += int((y_own.float() != y_roll.float()).sum().item())
+        n_all += r.numel()
+    out = {("guided_k%d" % k if nm == "guided" else nm): round(v / n_all, 6) for nm, v in tot.items()}
+    out["rtn_abs_index_step_hist"] = {str(i): int(v) for i, v in enumerate(hist.tolist()) if i and v}
     return out
 
 
@@ -148,61 +158,60 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    name, shape = synth.tensor_specs(WORKLOAD)[0]
-    sets = [synth.make_pair(WORKLOAD, 0, shape, dev)]
-    # a second, differently seeded input set: consecutive steps alternate, so
-    # no step finds its inputs in the 256 MB last-level cache
-    X2 = sets[0][0].roll(1, 0).contiguous()
-    Y2 = sets[0][1].roll(1, 0).contiguous()
-    sets.append((X2, Y2))
-    n = sets[0][0].numel()
-    k = K_BITS
-    gbytes2 = tq.guidance_bytes(n, k)
-    gbytes4 = tq.guidance_bytes(n, 4)
-    bufs = []
-    for _ in sets:
-        bufs.append(dict(
+    k = args.k
+    W = synth.WORKLOADS[args.workload]
+    specs = synth.tensor_specs(args.workload)
+    # two input sets per tensor (the second rolled along the leading dim):
+    # consecutive steps alternate, so no step finds its inputs in the 256 MB
+    # last-level cache
+    pairs = [synth.make_pair(args.workload, pos, shape, dev) for pos, (_, shape) in enumerate(specs)]
+    sets = [pairs, [(X.roll(1, 0).contiguous(), Y.roll(1, 0).contiguous()) for X, Y in pairs]]
+    ns = [X.numel() for X, _ in pairs]
+    n_total = sum(ns)
+
+    def make_bufs(shape, n):
+        return dict(
             g=torch.empty(1, dtype=torch.float32, device=dev),
             gx=torch.empty(1, dtype=torch.float32, device=dev),
             codes=torch.empty(n // 2, dtype=torch.uint8, device=dev),
             scales=torch.empty(n // 16, dtype=torch.uint8, device=dev),
-            gd=torch.empty(gbytes2, dtype=torch.uint8, device=dev),
-            gd4=torch.empty(gbytes4, dtype=torch.uint8, device=dev),
+            gd=torch.empty(tq.guidance_bytes(n, k), dtype=torch.uint8, device=dev),
+            gd4=torch.empty(tq.guidance_bytes(n, 4), dtype=torch.uint8, device=dev),
             y_g=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_f=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
-        ))
-    names = list(bytes_per_elem(k).keys())
+        )
+
+    bufs = [[make_bufs(shape, n) for (_, shape), n in zip(specs, ns)] for _ in range(2)]
 
     def launch(nm, i):
-        """One launch of step kernel `nm` on input set i % 2."""
-        X, Y = sets[i % 2]
-        b = bufs[i % 2]
-        if nm == "amax_rollout":
-            tq.amax(Y, out=b["g"])
-        elif nm == "quant_rollout":
-            tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
-        elif nm == "guidance_pack_full":
-            tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
-        elif nm == "fakequant_guided":
-            tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
-        elif nm == "fakequant_fullcode":
-            tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
-        elif nm == "amax_training":
-            tq.amax(X, out=b["gx"])
-        else:
-            tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
+        """Kernel `nm` once on every tensor of input set i % 2."""
+        for (X, Y), b, n in zip(sets[i % 2], bufs[i % 2], ns):
+            if nm == "amax_rollout":
+                tq.amax(Y, out=b["g"])
+            elif nm == "quant_rollout":
+                tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+            elif nm == "guidance_pack_full":
+                tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
+            elif nm == "fakequant_guided":
+                tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
+            elif nm == "fakequant_fullcode":
+                tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
+            elif nm == "amax_training":
+                tq.amax(X, out=b["gx"])
+            else:
+                tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
 
     def step(i):
-        for nm in names:
+        for nm in KERNELS:
             launch(nm, i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # The step is captured once per input set into a HIP graph (11 kernel
-    # launches, no memset/memcpy nodes) and replayed; eager launching is
+    # The step is captured once per input set into a HIP graph (kernel
+    # launches only, no memset/memcpy nodes) and replayed; eager launching is
     # timed too, for reference.
     graphs = []
     if not args.eager:
@@ -247,26 +256,25 @@ def main():
     # (a single launch between two events would also count the event's own
     # dispatch and release, ~2-4 us)
     per = {}
-    for nm in names:
+    for nm in KERNELS:
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(K):
             launch(nm, i)
         b_.record()
         torch.cuda.synchronize()
-        per[nm] = a.elapsed_time(b_) / K                   # ms per launch
+        per[nm] = a.elapsed_time(b_) / K                   # ms per launch of every tensor
 
     bpe = bytes_per_elem(k)
-    step_bytes = sum(bpe.values()) * n
+    step_bytes = sum(bpe.values()) * n_total
     value = step_bytes / (ms_step * 1e-3) / 1e9
-
     g_ms = per["fakequant_guided"]
-    g_bytes = bpe["fakequant_guided"] * n
+    g_bytes = bpe["fakequant_guided"] * n_total
     achieved = g_bytes / (g_ms * 1e-3) / 1e9
     kernels = {nm: {"us": round(per[nm] * 1e3, 2),
-                    "GBps": round(bpe[nm] * n / (per[nm] * 1e-3) / 1e9, 1),
-                    "frac_of_peak": round(bpe[nm] * n / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-               for nm in names}
+                    "GBps": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for nm in KERNELS}
 
     if args.calib_copy_mib:
         m = args.calib_copy_mib << 20
@@ -276,16 +284,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    b = bufs[0]
-    X, Y = sets[0]
     step(0)
-    mism = mismatch_stats(tq, X, Y, b["g"], b["codes"], b["scales"], b["gd"], b["gd4"])
+    mism = mismatch_stats(tq, sets[0], bufs[0], k)
     torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(X, Y, min(args.cpu_elems, n))
+        X, Y = pairs[0]
+        cpu = cpu_baseline(X, Y, min(args.cpu_elems, ns[0]), k)
 
+    default = args.workload == DEFAULT_WORKLOAD and k == 2
+    dist = {"normal_outliers": "N(0,1), 0.5% x20", "student_t4": "Student-t nu=4",
+            "kv": "LogNormal(0,0.5) per-channel scale x N(0,1)", "kv_outliers": "as KV plus 1% token rows x10",
+            "moe_step": "activations Student-t nu=3 + KV"}[W.dist]
     out = {
         "metric": "guided FP4 fake-quant GB/s and % of HBM peak on 1 MI355X; mismatch rate",
         "value": round(value, 1),
@@ -302,12 +313,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "routed-expert activations 64x512x2048 bf16 (Student-t nu=4, rollout "
-                               "relative noise 0.01), k=2 guidance, G=1, whole rollout+training step",
-                   "elements": n, "k": k, "G": 1, "step_bytes": int(step_bytes)},
+        "config": {"workload": f"{W.name} bf16 ({dist}, rollout relative noise {W.rel_noise}), k={k} "
+                               "guidance, G=1, whole rollout+training step",
+                   "tensors": [f"{nm} {'x'.join(map(str, sh))}" for nm, sh in specs],
+                   "elements": n_total, "k": k, "G": 1, "step_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
-                     "kernel": "k_fakequant_guided<2,true,false> (trace_fakequant_guided, k=2, bf16 out)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,
+                     "kernel": f"k_fakequant_guided<{k},true,false> (trace_fakequant_guided, k={k}, bf16 out)",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "mismatch": mism,

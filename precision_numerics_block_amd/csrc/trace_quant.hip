@@ -61,16 +61,30 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef TRACE_NT_STORE
 #define TRACE_NT_STORE 0
 #endif
+#ifndef TRACE_PAIR_SPLIT
+#define TRACE_PAIR_SPLIT 1
+#endif
+
 
 constexpr int kThreads = 256;          // 4 wavefronts of 64
 constexpr int kUnroll = TRACE_UNROLL;  // chunks per thread per tile
 constexpr int kTile = kThreads * kUnroll;
 constexpr int kMaxGrid = TRACE_WG_PER_CU > 0 ? 256 * TRACE_WG_PER_CU : 0x7fffffff;
-constexpr int kAmaxThreads = 1024;     // amax: one large workgroup per CU ...
-constexpr int kAmaxUnroll = 4;         // ... with 64 bytes in flight per lane
+#ifndef TRACE_AMAX_THREADS
+#define TRACE_AMAX_THREADS 1024
+#endif
+#ifndef TRACE_AMAX_UNROLL
+#define TRACE_AMAX_UNROLL 4
+#endif
+#ifndef TRACE_AMAX_GRID
+#define TRACE_AMAX_GRID 256
+#endif
+constexpr int kAmaxThreads = TRACE_AMAX_THREADS;   // amax: workgroup size ...
+constexpr int kAmaxUnroll = TRACE_AMAX_UNROLL;     // ... chunks in flight per lane ...
 constexpr int kAmaxTile = kAmaxThreads * kAmaxUnroll;
-constexpr int kAmaxGrid = 256;
+constexpr int kAmaxGrid = TRACE_AMAX_GRID;         // ... and persistent grid
 constexpr int kBuckets = 11;           // buckets of |v| (see decide)
+static_assert(!TRACE_PAIR_SPLIT || kUnroll == 2, "the lane-pair split of the block-scale work needs two chunks per lane");
 constexpr int kSlots = 16;             // table slots per row (bucket -> slot)
 
 // ---------------------------------------------------------------------------
@@ -291,6 +305,56 @@ __device__ __forceinline__ uint32_t chunk_amax_bits(const Chunk &x)
 __device__ __forceinline__ uint32_t pair_max(uint32_t m)
 {
     return max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xb1, 0xf, 0xf, false));
+}
+
+// Value of the neighbour lane (lane ^ 1).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false);
+}
+
+// Per-block scale work of a lane's two chunks (u = 0, 1), split across the
+// lane pair that shares their two blocks: the even lane derives block 0, the
+// odd lane block 1, and one DPP swap per value hands each lane the other.
+struct PairScales {
+    uint32_t sc[2];
+    float s[2], inv[2];
+};
+
+__device__ __forceinline__ PairScales pair_scales_from_amax(uint32_t ab0, uint32_t ab1, float g0, float g1)
+{
+    bool odd = threadIdx.x & 1u;
+    float gm = odd ? g1 : g0;
+    uint32_t sc = block_scale(as_f((odd ? ab1 : ab0) << 16), gm);
+    float s = e4m3_decode(sc);
+    float inv = inv_combined(s, gm);
+    uint32_t sc_o = pair_swap(sc), s_o = pair_swap(as_u(s)), inv_o = pair_swap(as_u(inv));
+    PairScales r;
+    r.sc[0] = odd ? sc_o : sc;
+    r.sc[1] = odd ? sc : sc_o;
+    r.s[0] = odd ? as_f(s_o) : s;
+    r.s[1] = odd ? s : as_f(s_o);
+    r.inv[0] = odd ? as_f(inv_o) : inv;
+    r.inv[1] = odd ? inv : as_f(inv_o);
+    return r;
+}
+
+__device__ __forceinline__ PairScales pair_scales_from_bytes(uint32_t sc0, uint32_t sc1, float g0, float g1)
+{
+    bool odd = threadIdx.x & 1u;
+    float gm = odd ? g1 : g0;
+    uint32_t sc = (odd ? sc1 : sc0) & 0x7fu;
+    float s = e4m3_decode(sc);
+    float inv = inv_combined(s, gm);
+    uint32_t s_o = pair_swap(as_u(s)), inv_o = pair_swap(as_u(inv));
+    PairScales r;
+    r.sc[0] = sc0 & 0x7fu;
+    r.sc[1] = sc1 & 0x7fu;
+    r.s[0] = odd ? as_f(s_o) : s;
+    r.s[1] = odd ? s : as_f(s_o);
+    r.inv[0] = odd ? as_f(inv_o) : inv;
+    r.inv[1] = odd ? inv : as_f(inv_o);
+    return r;
 }
 
 // k low bits of each of 8 nibbles of w, packed LSB-first (k = 1 or 2).
@@ -517,32 +581,57 @@ __global__ void __launch_bounds__(kThreads)
         uint32_t cs[kUnroll];
         for (int u = 0; u < kUnroll; ++u) {
             cs[u] = t * kTile + u * kThreads + threadIdx.x;
-            if (cs[u] < nchunk)
-                xc[u] = load_chunk(y, cs[u]);
+            xc[u] = cs[u] < nchunk ? load_chunk(y, cs[u]) : Chunk{{0u, 0u, 0u, 0u}};
         }
+        if (cs[0] >= nchunk)                       // later chunks of this lane are further out
+            continue;
+        uint32_t sc[kUnroll];
+        float inv[kUnroll];
+        float gg[kUnroll];
+        for (int u = 0; u < kUnroll; ++u)
+            gg[u] = group_scale<kOneGroup>(g, cs[u] >> 1, dm, last_group);
+#if TRACE_PAIR_SPLIT
+        PairScales ps = pair_scales_from_amax(pair_max(chunk_amax_bits(xc[0])), pair_max(chunk_amax_bits(xc[1])),
+                                              gg[0], gg[1]);
+        for (int u = 0; u < kUnroll; ++u) {
+            sc[u] = ps.sc[u];
+            inv[u] = ps.inv[u];
+        }
+        {   // each lane writes the scale byte of the block it derived
+            int mine = threadIdx.x & 1;
+            uint32_t c = cs[mine];
+            if (c < nchunk) {
+                scales[c >> 1] = (uint8_t)sc[mine];
+                if (gd_scales)
+                    gd_scales[c >> 1] = (uint8_t)sc[mine];
+            }
+        }
+#else
+        for (int u = 0; u < kUnroll; ++u) {
+            sc[u] = block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg[u]);
+            inv[u] = inv_combined(e4m3_decode(sc[u]), gg[u]);
+            if (cs[u] < nchunk && (cs[u] & 1u) == 0) {
+                scales[cs[u] >> 1] = (uint8_t)sc[u];
+                if (gd_scales)
+                    gd_scales[cs[u] >> 1] = (uint8_t)sc[u];
+            }
+        }
+#endif
         for (int u = 0; u < kUnroll; ++u) {
             uint32_t c = cs[u];
             if (c >= nchunk)
                 continue;
-            uint32_t blk = c >> 1;
-            float gg = group_scale<kOneGroup>(g, blk, dm, last_group);
-            uint32_t ab = pair_max(chunk_amax_bits(xc[u]));
-            uint32_t sc = block_scale(as_f(ab << 16), gg);
-            float inv = inv_combined(e4m3_decode(sc), gg);
-            uint32_t cw = rtn8(xc[u], inv);
+            uint32_t cw = rtn8(xc[u], inv[u]);
             st_stream(cw, codes + c);
-            if ((c & 1u) == 0) {
-                scales[blk] = (uint8_t)sc;
-                if (gd_scales)
-                    gd_scales[blk] = (uint8_t)sc;
-            }
             if (gd_scales)
                 store_bits<K>(gd_bits, c, cw);
         }
     }
 }
 
-// Guidance stream from codes + scales.
+// Guidance stream from codes + scales.  Each lane packs four chunks (two
+// blocks): one 16-byte code load, one 2-byte scale load, and one store per
+// plane; a trailing pair of chunks (n % 32 == 16) takes a narrow path.
 template <int K>
 __global__ void __launch_bounds__(kThreads)
     k_guidance_pack(const uint32_t *__restrict__ codes, const uint8_t *__restrict__ scales, uint32_t nchunk,
@@ -550,11 +639,24 @@ __global__ void __launch_bounds__(kThreads)
                     uint32_t pad_end)
 {
     zero_pad(gd_scales, pad_begin, pad_end);
-    for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < nchunk; c += gridDim.x * kThreads) {
-        uint32_t cw = ld_stream(codes + c);
-        if ((c & 1u) == 0)
-            gd_scales[c >> 1] = scales[c >> 1];
-        store_bits<K>(gd_bits, c, cw);
+    uint32_t q = blockIdx.x * kThreads + threadIdx.x;     // quad of chunks
+    uint32_t c = 4 * q;
+    if (c + 4 <= nchunk) {
+        u32x4 cw = ld_stream(reinterpret_cast<const u32x4 *>(codes) + q);
+        reinterpret_cast<uint16_t *>(gd_scales)[q] = reinterpret_cast<const uint16_t *>(scales)[q];
+        if (K == 4) {
+            reinterpret_cast<u32x4 *>(gd_bits)[q] = cw;
+        } else if (K == 2) {
+            u32x2 b = {compact_k2(cw.x) | (compact_k2(cw.y) << 16), compact_k2(cw.z) | (compact_k2(cw.w) << 16)};
+            reinterpret_cast<u32x2 *>(gd_bits)[q] = b;
+        } else {
+            reinterpret_cast<uint32_t *>(gd_bits)[q] = compact_k1(cw.x) | (compact_k1(cw.y) << 8) |
+                                                       (compact_k1(cw.z) << 16) | (compact_k1(cw.w) << 24);
+        }
+    } else if (c < nchunk) {                                 // the last two chunks: one block
+        gd_scales[c >> 1] = scales[c >> 1];
+        store_bits<K>(gd_bits, c, codes[c]);
+        store_bits<K>(gd_bits, c + 1, codes[c + 1]);
     }
 }
 
@@ -575,6 +677,9 @@ __global__ void __launch_bounds__(kThreads)
         for (int u = 0; u < kUnroll; ++u) {
             uint32_t c = t * kTile + u * kThreads + threadIdx.x;
             cs[u] = c;
+            xc[u] = Chunk{{0u, 0u, 0u, 0u}};
+            sc[u] = 0u;
+            gb[u] = 0u;
             if (c < nchunk) {
                 xc[u] = load_chunk(x, c);
                 sc[u] = scale_plane[c >> 1];
@@ -586,18 +691,32 @@ __global__ void __launch_bounds__(kThreads)
                     gb[u] = ld_stream(reinterpret_cast<const uint32_t *>(bits) + c);
             }
         }
+        if (cs[0] >= nchunk)
+            continue;
+        float gg[kUnroll], s[kUnroll], inv[kUnroll];
+        for (int u = 0; u < kUnroll; ++u)
+            gg[u] = group_scale<kOneGroup>(g, cs[u] >> 1, dm, last_group);
+#if TRACE_PAIR_SPLIT
+        PairScales ps = pair_scales_from_bytes(sc[0], sc[1], gg[0], gg[1]);
+        for (int u = 0; u < kUnroll; ++u) {
+            s[u] = ps.s[u];
+            inv[u] = ps.inv[u];
+        }
+#else
+        for (int u = 0; u < kUnroll; ++u) {
+            s[u] = e4m3_decode(sc[u] & 0x7fu);
+            inv[u] = inv_combined(s[u], gg[u]);
+        }
+#endif
         for (int u = 0; u < kUnroll; ++u) {
             uint32_t c = cs[u];
             if (c >= nchunk)
                 continue;
-            float gg = group_scale<kOneGroup>(g, c >> 1, dm, last_group);
-            float s = e4m3_decode(sc[u] & 0x7fu);
-            float inv = inv_combined(s, gg);
             float yv[8];
             uint32_t nw = 0;
             for (int i = 0; i < 8; ++i) {
                 uint32_t w = xc[u].w[i >> 1];
-                float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * inv;
+                float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * inv[u];
                 uint32_t row, nib = 0;
                 bool allow = true;
                 if (MODE == 1) {
@@ -609,7 +728,7 @@ __global__ void __launch_bounds__(kThreads)
                     row = r & 7u;
                     allow = (r >> 3) == (as_u(v) >> 31);
                 }
-                yv[i] = decide<R, kCodes>(tab, v, row, allow, s, gg, nib);
+                yv[i] = decide<R, kCodes>(tab, v, row, allow, s[u], gg[u], nib);
                 if (kCodes)
                     nw |= nib << (4 * i);
             }
@@ -635,30 +754,54 @@ __global__ void __launch_bounds__(kThreads)
         for (int u = 0; u < kUnroll; ++u) {
             uint32_t c = t * kTile + u * kThreads + threadIdx.x;
             cs[u] = c;
+            xc[u] = Chunk{{0u, 0u, 0u, 0u}};
+            sc[u] = 0u;
             if (c < nchunk) {
                 xc[u] = load_chunk(x, c);
                 if (!kOwn)
                     sc[u] = scales_in[c >> 1];
             }
         }
+        if (cs[0] >= nchunk)
+            continue;
+        float gg[kUnroll], s[kUnroll], inv[kUnroll];
+        for (int u = 0; u < kUnroll; ++u)
+            gg[u] = group_scale<kOneGroup>(g, cs[u] >> 1, dm, last_group);
+#if TRACE_PAIR_SPLIT
+        PairScales ps = kOwn ? pair_scales_from_amax(pair_max(chunk_amax_bits(xc[0])),
+                                                     pair_max(chunk_amax_bits(xc[1])), gg[0], gg[1])
+                             : pair_scales_from_bytes(sc[0], sc[1], gg[0], gg[1]);
+        for (int u = 0; u < kUnroll; ++u) {
+            sc[u] = ps.sc[u];
+            s[u] = ps.s[u];
+            inv[u] = ps.inv[u];
+        }
+        if (kOwn && scales_out) {                  // each lane writes the block it derived
+            int mine = threadIdx.x & 1;
+            if (cs[mine] < nchunk)
+                scales_out[cs[mine] >> 1] = (uint8_t)sc[mine];
+        }
+#else
+        for (int u = 0; u < kUnroll; ++u) {
+            sc[u] = kOwn ? block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg[u]) : (sc[u] & 0x7fu);
+            s[u] = e4m3_decode(sc[u]);
+            inv[u] = inv_combined(s[u], gg[u]);
+            if (kOwn && scales_out && cs[u] < nchunk && (cs[u] & 1u) == 0)
+                scales_out[cs[u] >> 1] = (uint8_t)sc[u];
+        }
+#endif
         for (int u = 0; u < kUnroll; ++u) {
             uint32_t c = cs[u];
             if (c >= nchunk)
                 continue;
-            float gg = group_scale<kOneGroup>(g, c >> 1, dm, last_group);
-            uint32_t s8 = kOwn ? block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg) : (sc[u] & 0x7fu);
-            float s = e4m3_decode(s8);
-            float inv = inv_combined(s, gg);
-            uint32_t cw = rtn8(xc[u], inv);
+            uint32_t cw = rtn8(xc[u], inv[u]);
             float yv[8];
             decode8(cw, yv);
             for (int i = 0; i < 8; ++i)
-                yv[i] = (yv[i] * s) * gg;               // signed value: the sign rides along
+                yv[i] = (yv[i] * s[u]) * gg[u];         // signed value: the sign rides along
             store_y(out, c, yv);
             if (kCodes)
                 st_stream(cw, codes_out + c);
-            if (kOwn && scales_out && (c & 1u) == 0)
-                scales_out[c >> 1] = (uint8_t)s8;
         }
     }
 }
@@ -849,9 +992,8 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
     if (k != 1 && k != 2 && k != 4)
         return TRACE_E_K;
     uint32_t nchunk = (uint32_t)(n / 8);
-    uint32_t wgs = (nchunk + kThreads - 1) / kThreads;
-    const uint32_t pack_grid = 256 * 8;                  // persistent: 8 workgroups per CU
-    dim3 grid(wgs < pack_grid ? wgs : pack_grid);
+    uint32_t nquad = (nchunk + 3) / 4;
+    dim3 grid((nquad + kThreads - 1) / kThreads);
     hipStream_t st = (hipStream_t)stream;
     uint8_t *bits = guidance + bitplane_offset(n);
     uint32_t pb = (uint32_t)(n / 16), pe = (uint32_t)bitplane_offset(n);
