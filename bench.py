@@ -145,6 +145,99 @@ def mismatch_stats(tq, pairs, bufs, k):
     return out
 
 
+def transport_stats(tq, graphs, sets, bufs, ns, K, k):
+    """Guidance transport ("TRACE Core Concept": the guidance travels GPU ->
+    CPU memory -> disk -> CPU -> GPU): per-stage rates for the compact (k)
+    and the full-code stream of the first tensor, and the step time when the
+    previous step's stream is copied to pinned host memory on a side stream
+    while the step runs."""
+    import tempfile
+
+    import torch
+
+    out = {}
+    n = ns[0]
+    main = torch.cuda.current_stream()
+    for label, kk, key in ((f"compact_k{k}", k, "gd"), ("full_k4", 4, "gd4")):
+        b = bufs[0][0]
+        rec = torch.empty(tq.record_bytes(n, kk), dtype=torch.uint8, pin_memory=True)
+        gd2 = torch.empty_like(b[key])
+        g2 = torch.empty_like(b["g"])
+        reps = 10
+        for _ in range(3):                               # first touch of the pinned pages
+            tq.record_to_host(b[key], b["g"], n, kk, out=rec)
+            tq.record_from_host(rec, gd2, g2)
+        torch.cuda.synchronize()
+        tq.record_seal(rec)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        for _ in range(reps):
+            tq.record_to_host(b[key], b["g"], n, kk, out=rec)
+        e1.record()
+        for _ in range(reps):
+            tq.record_from_host(rec, gd2, g2)
+        e2.record()
+        torch.cuda.synchronize()
+        d2h = e0.elapsed_time(e1) / reps * 1e-3
+        h2d = e1.elapsed_time(e2) / reps * 1e-3
+        t = time.perf_counter()
+        tq.record_seal(rec)
+        t_seal = time.perf_counter() - t
+        with tempfile.TemporaryDirectory() as d:
+            path = os.path.join(d, "guidance.trg")
+            back = torch.empty(rec.numel(), dtype=torch.uint8, pin_memory=True)
+            tq.record_write(path, rec)
+            tq.record_read(path, rec.numel(), out=back)      # warm: page cache and pinned pages
+            t = time.perf_counter()
+            tq.record_write(path, rec)
+            t_w = time.perf_counter() - t
+            t = time.perf_counter()
+            back = tq.record_read(path, rec.numel(), out=back)
+            t_r = time.perf_counter() - t
+            t = time.perf_counter()
+            ok = tq.record_check(back) == (n, kk, 1)
+            t_chk = time.perf_counter() - t
+        nb = rec.numel()
+        out[label] = {"record_bytes": nb, "bits_per_element": round(8 * nb / n, 4),
+                      "d2h_GBps": round(nb / d2h / 1e9, 2), "h2d_GBps": round(nb / h2d / 1e9, 2),
+                      "seal_GBps": round(nb / t_seal / 1e9, 2), "file_write_GBps": round(nb / t_w / 1e9, 2),
+                      "file_read_GBps": round(nb / t_r / 1e9, 2), "check_GBps": round(nb / t_chk / 1e9, 2),
+                      "round_trip_ok": bool(ok and torch.equal(gd2, b[key]))}
+
+    if not graphs:
+        return out
+    side = torch.cuda.Stream()
+
+    def run(key, kk):
+        recs = [torch.empty(tq.record_bytes(n, kk), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        done_step = [torch.cuda.Event() for _ in range(2 * K)]
+        done_copy = [torch.cuda.Event() for _ in range(2 * K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(2 * K):                          # first K steps warm the pinned pages
+            if i == K:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            if key and i >= 2:
+                main.wait_event(done_copy[i - 2])      # set i % 2 is rewritten only after its copy
+            graphs[i % 2].replay()
+            done_step[i].record(main)
+            if key:
+                with torch.cuda.stream(side):
+                    side.wait_event(done_step[i])
+                    b = bufs[i % 2][0]
+                    tq.record_to_host(b[key], b["g"], n, kk, out=recs[i % 2])
+                    done_copy[i].record(side)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    base = run(None, k)
+    out["step_ms"] = round(base, 4)
+    out[f"step_ms_with_d2h_compact_k{k}"] = round(run("gd", k), 4)
+    out["step_ms_with_d2h_full_k4"] = round(run("gd4", 4), 4)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,6 +380,7 @@ def main():
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k)
     torch.cuda.synchronize()
+    transport = transport_stats(tq, graphs, sets, bufs, ns, min(K, 20), k)
 
     cpu = None
     if not args.no_cpu:
@@ -324,6 +418,7 @@ def main():
         "cpu_baseline": cpu,
         "mismatch": mism,
         "kernels": kernels,
+        "transport": transport,
     }
     print(json.dumps(out))
 

@@ -70,7 +70,9 @@ typedef enum {
     TRACE_E_K = -4,         /* unsupported guidance width */
     TRACE_E_DTYPE = -5,     /* unknown output dtype */
     TRACE_E_HIP = -6,       /* the HIP runtime reported an error */
-    TRACE_E_NONFINITE = -7  /* (device status word) an input was inf/NaN */
+    TRACE_E_NONFINITE = -7, /* (device status word) an input was inf/NaN */
+    TRACE_E_FORMAT = -8,    /* a guidance record fails its header or hash check */
+    TRACE_E_IO = -9         /* a file could not be opened, written or read */
 } trace_status;
 
 typedef enum { TRACE_OUT_BF16 = 0, TRACE_OUT_F32 = 1 } trace_out_dtype;
@@ -134,6 +136,55 @@ int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *
  * scale RTN).  codes_out (u8[n/2]) and scales_out (u8[n/16]) are nullable. */
 int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales_in,
                         void *y_out, int out_dtype, uint8_t *codes_out, uint8_t *scales_out, void *stream);
+
+/* ---- guidance records (transport and persistence) ---------------------- */
+/*
+ * "TRACE Core Concept": the rollout's guidance travels GPU -> CPU memory ->
+ * disk -> CPU -> GPU before the training step uses it, and long trajectories,
+ * large batches and async RL raise that cost; "Experimental Results": full
+ * guidance slows rollout badly, the compact form stays close to plain FP4.
+ *
+ * A record is one self-describing host buffer:
+ *   bytes  0..63   header (little-endian): magic 0x44475254 ("TRGD") (u32),
+ *                  version 1 (u32), n (i64), k (i32), G (i32), stream bytes
+ *                  (u64), bit-plane offset (u64), payload bytes (u64), XXH64
+ *                  of the payload (u64), sealed flag (u32), zero pad to 64
+ *   bytes 64..     payload: g (f32[G]) zero-padded to a multiple of 64 bytes,
+ *                  then the guidance stream (trace_guidance_bytes(n, k))
+ * The hash is XXH64 (seed 0) of the whole payload.  Host pointers below may
+ * point to any host memory; for asynchronous copies it should be pinned
+ * (hipHostMalloc or a pinned torch tensor).  The caller owns every buffer.
+ */
+
+/* Total record size for (n, k, G); 0 for invalid arguments. */
+size_t trace_record_bytes(int64_t n, int k, int G);
+
+/* Writes the header (unsealed) into record_host now and enqueues the
+ * device-to-host copies of g (device f32[G]) and the guidance stream (device)
+ * on `stream`.  Call trace_record_seal once the stream has passed the copies. */
+int trace_record_to_host(const uint8_t *guidance, const float *g, int64_t n, int k, int G,
+                         void *record_host, size_t record_bytes, void *stream);
+
+/* Host only: hashes the payload into the header and marks it sealed. */
+int trace_record_seal(void *record_host, size_t record_bytes);
+
+/* Host only: validates magic, version, sizes, the sealed flag and the hash;
+ * returns TRACE_OK and (if not NULL) n, k, G, or TRACE_E_FORMAT. */
+int trace_record_check(const void *record_host, size_t record_bytes, int64_t *n, int *k, int *G);
+
+/* Validates the header (not the hash: call trace_record_check for that) and
+ * enqueues the host-to-device copies of g and the stream on `stream`. */
+int trace_record_from_host(const void *record_host, size_t record_bytes, uint8_t *guidance, float *g,
+                           void *stream);
+
+/* Host only: whole-record file write / read (POSIX).  read fills at most
+ * `capacity` bytes and reports the record size in *bytes_read; it fails with
+ * TRACE_E_FORMAT when the file is not a record or does not fit. */
+int trace_record_write(const char *path, const void *record_host, size_t record_bytes);
+int trace_record_read(const char *path, void *record_host, size_t capacity, size_t *bytes_read);
+
+/* Host only: XXH64 (seed 0) of a host buffer, the hash records use. */
+uint64_t trace_xxh64(const void *data, size_t bytes);
 
 /* ---- misc --------------------------------------------------------------- */
 

@@ -5,7 +5,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "trace_quant.hip")
+SRCS = [os.path.join(HERE, "csrc", "trace_quant.hip"), os.path.join(HERE, "csrc", "trace_record.cpp")]
 OUT = os.path.join(HERE, "libtrace_quant.so")
 
 HIPCC_FLAGS = [
@@ -19,7 +19,7 @@ HIPCC_FLAGS = [
 def build(verbose=False):
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)

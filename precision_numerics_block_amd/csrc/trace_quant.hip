@@ -1079,6 +1079,8 @@ const char *trace_status_str(int status)
     case TRACE_E_DTYPE: return "unknown output dtype";
     case TRACE_E_HIP: return "HIP runtime error";
     case TRACE_E_NONFINITE: return "an input was inf or NaN";
+    case TRACE_E_FORMAT: return "guidance record fails its header or hash check";
+    case TRACE_E_IO: return "file could not be opened, written or read";
     default: return "unknown status";
     }
 }

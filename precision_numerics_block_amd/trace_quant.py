@@ -31,6 +31,14 @@ _SIGS = {
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_rtn": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp]),
+    "trace_record_bytes": (_sz, [_i64, _int, _int]),
+    "trace_record_to_host": (_int, [_vp, _vp, _i64, _int, _int, _vp, _sz, _vp]),
+    "trace_record_seal": (_int, [_vp, _sz]),
+    "trace_record_check": (_int, [_vp, _sz, ctypes.POINTER(_i64), ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "trace_record_from_host": (_int, [_vp, _sz, _vp, _vp, _vp]),
+    "trace_record_write": (_int, [ctypes.c_char_p, _vp, _sz]),
+    "trace_record_read": (_int, [ctypes.c_char_p, _vp, _sz, ctypes.POINTER(_sz)]),
+    "trace_xxh64": (ctypes.c_uint64, [_vp, _sz]),
     "trace_status_str": (ctypes.c_char_p, [_int]),
     "trace_version": (_int, []),
 }
@@ -44,6 +52,8 @@ OUT_BF16, OUT_F32 = 0, 1
 __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
+    "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
+    "record_read", "xxh64",
 ]
 
 
@@ -179,3 +189,74 @@ def fakequant_rtn(x, g, scales_in=None, G=1, out_dtype=OUT_BF16, out=None, codes
         _ptr(x), x.numel(), int(G), _ptr(g), _ptr(scales_in), _ptr(out), int(out_dtype),
         _ptr(codes_out), _ptr(scales_out), _stream(x.device)))
     return out, codes_out, scales_out
+
+
+# ---- guidance records (transport and persistence) -------------------------
+def record_bytes(n, k, G=1):
+    return int(lib.trace_record_bytes(int(n), int(k), int(G)))
+
+
+def _host_ptr(buf):
+    if isinstance(buf, torch.Tensor):
+        if buf.is_cuda or buf.dtype != torch.uint8 or not buf.is_contiguous():
+            raise TypeError("record buffers are contiguous uint8 host tensors")
+        return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+    raise TypeError("record buffers are uint8 host tensors")
+
+
+def record_to_host(guidance, g, n, k, G=1, out=None):
+    """Enqueue the device->host copy of a guidance stream and its global
+    scales into a record (a pinned uint8 host tensor, allocated when `out` is
+    None).  Synchronise the stream, then call record_seal."""
+    _need(guidance, torch.uint8, "guidance")
+    _need(g, torch.float32, "g")
+    if out is None:
+        out = torch.empty(record_bytes(n, k, G), dtype=torch.uint8, pin_memory=True)
+    p, nb = _host_ptr(out)
+    _check("trace_record_to_host", lib.trace_record_to_host(
+        _ptr(guidance), _ptr(g), int(n), int(k), int(G), p, nb, _stream(guidance.device)))
+    return out
+
+
+def record_seal(record):
+    p, nb = _host_ptr(record)
+    _check("trace_record_seal", lib.trace_record_seal(p, nb))
+
+
+def record_check(record):
+    """(n, k, G) of a sealed, intact record; raises TraceError otherwise."""
+    p, nb = _host_ptr(record)
+    n, k, G = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
+    _check("trace_record_check", lib.trace_record_check(p, nb, ctypes.byref(n), ctypes.byref(k), ctypes.byref(G)))
+    return n.value, k.value, G.value
+
+
+def record_from_host(record, guidance, g, device=None):
+    """Enqueue the host->device copy of a record into `guidance` and `g`."""
+    _need(guidance, torch.uint8, "guidance")
+    _need(g, torch.float32, "g")
+    p, nb = _host_ptr(record)
+    _check("trace_record_from_host", lib.trace_record_from_host(
+        p, nb, _ptr(guidance), _ptr(g), _stream(guidance.device)))
+    return guidance, g
+
+
+def record_write(path, record):
+    p, nb = _host_ptr(record)
+    _check("trace_record_write", lib.trace_record_write(str(path).encode(), p, nb))
+
+
+def record_read(path, capacity, out=None):
+    """Read a record file into a pinned host tensor of `capacity` bytes;
+    returns the tensor trimmed to the record's size."""
+    if out is None:
+        out = torch.empty(int(capacity), dtype=torch.uint8, pin_memory=True)
+    p, nb = _host_ptr(out)
+    got = ctypes.c_size_t()
+    _check("trace_record_read", lib.trace_record_read(str(path).encode(), p, nb, ctypes.byref(got)))
+    return out[: got.value]
+
+
+def xxh64(buf):
+    p, nb = _host_ptr(buf)
+    return int(lib.trace_xxh64(p, nb))
