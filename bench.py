@@ -295,6 +295,8 @@ def main():
             else:
                 tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
 
+    # One stream: running the independent plain-QAT chain (amax(X) -> RTN) on
+    # a second stream was measured slower (two HBM-bound chains interfere).
     def step(i):
         for nm in KERNELS:
             launch(nm, i)
