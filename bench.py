@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--k", type=int, default=2, choices=[1, 2], help="guidance bits of the compact stream")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
+    p.add_argument("--separate-kv", action="store_true",
+                   help="K and V as two tensors (G = 1 each) instead of one [2, T, H, D] buffer with G = 2")
     p.add_argument("--cpu-elems", type=int, default=1 << 25, help="oracle sample size (elements)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain copy of this size (for counter calibration)")
@@ -110,7 +112,7 @@ def cpu_baseline(X, Y, n_sample, k):
                       f"single-threaded C"}
 
 
-def mismatch_stats(tq, pairs, bufs, k):
+def mismatch_stats(tq, pairs, bufs, k, Gs):
     """Element-level code mismatch between the training side and the rollout
     codes, summed over the workload's tensors."""
     import torch
@@ -125,13 +127,13 @@ def mismatch_stats(tq, pairs, bufs, k):
     tot = {"rtn_shared_scale": 0, "guided": 0, "full_code": 0, "rtn_own_scale_value": 0}
     hist = torch.zeros(8, dtype=torch.int64, device=pairs[0][0].device)
     n_all = 0
-    for (X, Y), b in zip(pairs, bufs):
+    for (X, Y), b, G in zip(pairs, bufs, Gs):
         r = signed(b["codes"])
-        _, c_rtn, _ = tq.fakequant_rtn(X, b["g"], b["scales"], codes_out=True)
-        _, c_gd = tq.fakequant_guided(X, b["g"], b["gd"], k, codes_out=True)
-        _, c_fc = tq.fakequant_fullcode(X, b["g"], b["gd4"], codes_out=True)
-        y_own, _, _ = tq.fakequant_rtn(X, b["gx"])
-        y_roll, _, _ = tq.fakequant_rtn(Y, b["g"], b["scales"])   # the rollout's dequantised values
+        _, c_rtn, _ = tq.fakequant_rtn(X, b["g"], b["scales"], G, codes_out=True)
+        _, c_gd = tq.fakequant_guided(X, b["g"], b["gd"], k, G, codes_out=True)
+        _, c_fc = tq.fakequant_fullcode(X, b["g"], b["gd4"], G, codes_out=True)
+        y_own, _, _ = tq.fakequant_rtn(X, b["gx"], None, G)
+        y_roll, _, _ = tq.fakequant_rtn(Y, b["g"], b["scales"], G)   # the rollout's dequantised values
         for name, c in (("rtn_shared_scale", c_rtn), ("guided", c_gd), ("full_code", c_fc)):
             d = signed(c) - r
             tot[name] += int((d != 0).sum().item())
@@ -145,7 +147,7 @@ def mismatch_stats(tq, pairs, bufs, k):
     return out
 
 
-def transport_stats(tq, graphs, sets, bufs, ns, K, k):
+def transport_stats(tq, graphs, sets, bufs, ns, Gs, K, k):
     """Guidance transport ("TRACE Core Concept": the guidance travels GPU ->
     CPU memory -> disk -> CPU -> GPU): per-stage rates for the compact (k)
     and the full-code stream of the first tensor, and the step time when the
@@ -156,23 +158,23 @@ def transport_stats(tq, graphs, sets, bufs, ns, K, k):
     import torch
 
     out = {}
-    n = ns[0]
+    n, G = ns[0], Gs[0]
     main = torch.cuda.current_stream()
     for label, kk, key in ((f"compact_k{k}", k, "gd"), ("full_k4", 4, "gd4")):
         b = bufs[0][0]
-        rec = torch.empty(tq.record_bytes(n, kk), dtype=torch.uint8, pin_memory=True)
+        rec = torch.empty(tq.record_bytes(n, kk, G), dtype=torch.uint8, pin_memory=True)
         gd2 = torch.empty_like(b[key])
         g2 = torch.empty_like(b["g"])
         reps = 10
         for _ in range(3):                               # first touch of the pinned pages
-            tq.record_to_host(b[key], b["g"], n, kk, out=rec)
+            tq.record_to_host(b[key], b["g"], n, kk, G, out=rec)
             tq.record_from_host(rec, gd2, g2)
         torch.cuda.synchronize()
         tq.record_seal(rec)
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record()
         for _ in range(reps):
-            tq.record_to_host(b[key], b["g"], n, kk, out=rec)
+            tq.record_to_host(b[key], b["g"], n, kk, G, out=rec)
         e1.record()
         for _ in range(reps):
             tq.record_from_host(rec, gd2, g2)
@@ -195,7 +197,7 @@ def transport_stats(tq, graphs, sets, bufs, ns, K, k):
             back = tq.record_read(path, rec.numel(), out=back)
             t_r = time.perf_counter() - t
             t = time.perf_counter()
-            ok = tq.record_check(back) == (n, kk, 1)
+            ok = tq.record_check(back) == (n, kk, G)
             t_chk = time.perf_counter() - t
         nb = rec.numel()
         out[label] = {"record_bytes": nb, "bits_per_element": round(8 * nb / n, 4),
@@ -209,7 +211,7 @@ def transport_stats(tq, graphs, sets, bufs, ns, K, k):
     side = torch.cuda.Stream()
 
     def run(key, kk):
-        recs = [torch.empty(tq.record_bytes(n, kk), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        recs = [torch.empty(tq.record_bytes(n, kk, G), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         done_step = [torch.cuda.Event() for _ in range(2 * K)]
         done_copy = [torch.cuda.Event() for _ in range(2 * K)]
         torch.cuda.synchronize()
@@ -226,7 +228,7 @@ def transport_stats(tq, graphs, sets, bufs, ns, K, k):
                 with torch.cuda.stream(side):
                     side.wait_event(done_step[i])
                     b = bufs[i % 2][0]
-                    tq.record_to_host(b[key], b["g"], n, kk, out=recs[i % 2])
+                    tq.record_to_host(b[key], b["g"], n, kk, G, out=recs[i % 2])
                     done_copy[i].record(side)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / K
@@ -258,14 +260,26 @@ def main():
     # consecutive steps alternate, so no step finds its inputs in the 256 MB
     # last-level cache
     pairs = [synth.make_pair(args.workload, pos, shape, dev) for pos, (_, shape) in enumerate(specs)]
-    sets = [pairs, [(X.roll(1, 0).contiguous(), Y.roll(1, 0).contiguous()) for X, Y in pairs]]
+    Gs = [1] * len(pairs)
+    names_shapes = [(nm, tuple(shape)) for nm, shape in specs]
+    if not args.separate_kv and [nm for nm, _ in specs][-2:] == ["k", "v"]:
+        # K and V of a layer in one [2, T, H, D] buffer, one global-scale group
+        # each (G = 2): every kernel runs once over both, scales stay per tensor
+        (K, Ky), (V, Vy) = pairs[-2:]
+        pairs = pairs[:-2] + [(torch.stack([K, V]), torch.stack([Ky, Vy]))]
+        Gs = Gs[:-2] + [2]
+        names_shapes = names_shapes[:-2] + [("kv", (2,) + tuple(K.shape))]
+        del K, Ky, V, Vy
+    rd = lambda t: 1 if t.dim() == 4 else 0        # roll tokens / experts, never K against V  # noqa: E731
+    sets = [pairs, [(X.roll(1, rd(X)).contiguous(), Y.roll(1, rd(Y)).contiguous()) for X, Y in pairs]]
     ns = [X.numel() for X, _ in pairs]
     n_total = sum(ns)
+    shapes = [X.shape for X, _ in pairs]
 
-    def make_bufs(shape, n):
+    def make_bufs(shape, n, G):
         return dict(
-            g=torch.empty(1, dtype=torch.float32, device=dev),
-            gx=torch.empty(1, dtype=torch.float32, device=dev),
+            g=torch.empty(G, dtype=torch.float32, device=dev),
+            gx=torch.empty(G, dtype=torch.float32, device=dev),
             codes=torch.empty(n // 2, dtype=torch.uint8, device=dev),
             scales=torch.empty(n // 16, dtype=torch.uint8, device=dev),
             gd=torch.empty(tq.guidance_bytes(n, k), dtype=torch.uint8, device=dev),
@@ -275,25 +289,25 @@ def main():
             y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
         )
 
-    bufs = [[make_bufs(shape, n) for (_, shape), n in zip(specs, ns)] for _ in range(2)]
+    bufs = [[make_bufs(shape, n, G) for shape, n, G in zip(shapes, ns, Gs)] for _ in range(2)]
 
     def launch(nm, i):
         """Kernel `nm` once on every tensor of input set i % 2."""
-        for (X, Y), b, n in zip(sets[i % 2], bufs[i % 2], ns):
+        for (X, Y), b, n, G in zip(sets[i % 2], bufs[i % 2], ns, Gs):
             if nm == "amax_rollout":
-                tq.amax(Y, out=b["g"])
+                tq.amax(Y, G, out=b["g"])
             elif nm == "quant_rollout":
-                tq.quant_rollout(Y, b["g"], k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+                tq.quant_rollout(Y, b["g"], k, G, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
             elif nm == "guidance_pack_full":
                 tq.guidance_pack(b["codes"], b["scales"], n, 4, out=b["gd4"])
             elif nm == "fakequant_guided":
-                tq.fakequant_guided(X, b["g"], b["gd"], k, out=b["y_g"])
+                tq.fakequant_guided(X, b["g"], b["gd"], k, G, out=b["y_g"])
             elif nm == "fakequant_fullcode":
-                tq.fakequant_fullcode(X, b["g"], b["gd4"], out=b["y_f"])
+                tq.fakequant_fullcode(X, b["g"], b["gd4"], G, out=b["y_f"])
             elif nm == "amax_training":
-                tq.amax(X, out=b["gx"])
+                tq.amax(X, G, out=b["gx"])
             else:
-                tq.fakequant_rtn(X, b["gx"], out=b["y_r"])
+                tq.fakequant_rtn(X, b["gx"], None, G, out=b["y_r"])
 
     # One stream: running the independent plain-QAT chain (amax(X) -> RTN) on
     # a second stream was measured slower (two HBM-bound chains interfere).
@@ -380,9 +394,9 @@ def main():
         torch.cuda.synchronize()
 
     step(0)
-    mism = mismatch_stats(tq, sets[0], bufs[0], k)
+    mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
-    transport = transport_stats(tq, graphs, sets, bufs, ns, min(K, 20), k)
+    transport = transport_stats(tq, graphs, sets, bufs, ns, Gs, min(K, 20), k)
 
     cpu = None
     if not args.no_cpu:
@@ -410,9 +424,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{W.name} bf16 ({dist}, rollout relative noise {W.rel_noise}), k={k} "
-                               "guidance, G=1, whole rollout+training step",
-                   "tensors": [f"{nm} {'x'.join(map(str, sh))}" for nm, sh in specs],
-                   "elements": n_total, "k": k, "G": 1, "step_bytes": int(step_bytes)},
+                               f"guidance, G={max(Gs)}, whole rollout+training step",
+                   "tensors": [f"{nm} {'x'.join(map(str, sh))} G={G}" for (nm, sh), G in zip(names_shapes, Gs)],
+                   "elements": n_total, "k": k, "G": max(Gs), "step_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,
                      "kernel": f"k_fakequant_guided<{k},true,false> (trace_fakequant_guided, k={k}, bf16 out)",

@@ -77,9 +77,9 @@ constexpr int kMaxGrid = TRACE_WG_PER_CU > 0 ? 256 * TRACE_WG_PER_CU : 0x7ffffff
 #define TRACE_AMAX_UNROLL 4
 #endif
 #ifndef TRACE_AMAX_GRID
-#define TRACE_AMAX_GRID 256
+#define TRACE_AMAX_GRID 512
 #endif
-constexpr int kAmaxThreads = TRACE_AMAX_THREADS;   // amax: workgroup size ...
+constexpr int kAmaxThreads = TRACE_AMAX_THREADS;   // amax: two 1024-thread workgroups per CU ...
 constexpr int kAmaxUnroll = TRACE_AMAX_UNROLL;     // ... chunks in flight per lane ...
 constexpr int kAmaxTile = kAmaxThreads * kAmaxUnroll;
 constexpr int kAmaxGrid = TRACE_AMAX_GRID;         // ... and persistent grid

@@ -442,3 +442,53 @@ def test_graph_replay_matches_eager(tq):
         torch.cuda.synchronize()
         for t, r in zip(outs, ref):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
+
+
+def test_qat_autograd_wrappers(tq):
+    """Forward = the kernels (already pinned to the oracle above); backward =
+    the incoming gradient, unchanged (straight-through)."""
+    from precision_numerics_block_amd import qat
+
+    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
+    g = tq.amax(Y)
+    codes, scales, gd2 = tq.quant_rollout(Y, g, 2)
+    gd4 = tq.guidance_pack(codes, scales, X.numel(), 4)
+    gx = tq.amax(X)
+    cases = [
+        (lambda x: qat.guided_fake_quant(x, g, gd2, 2), lambda: tq.fakequant_guided(X, g, gd2, 2)[0]),
+        (lambda x: qat.fullcode_fake_quant(x, g, gd4), lambda: tq.fakequant_fullcode(X, g, gd4)[0]),
+        (lambda x: qat.rtn_fake_quant(x, gx), lambda: tq.fakequant_rtn(X, gx)[0]),
+        (lambda x: qat.rtn_fake_quant(x, g, scales), lambda: tq.fakequant_rtn(X, g, scales)[0]),
+    ]
+    for fwd, ref in cases:
+        x = X.clone().requires_grad_(True)
+        y = fwd(x)
+        assert torch.equal(y.view(torch.int16), ref().view(torch.int16))
+        gy = torch.randn_like(y)
+        y.backward(gy)
+        assert torch.equal(x.grad, gy)
+    # a tiny training step through the guided fake-quant
+    w = torch.randn(2048, 64, device=DEV, dtype=torch.float32, requires_grad=True)
+    x = X.clone().requires_grad_(True)
+    loss = (qat.guided_fake_quant(x, g, gd2, 2).float() @ w).square().mean()
+    loss.backward()
+    assert torch.isfinite(w.grad).all() and x.grad is not None and torch.isfinite(x.grad.float()).all()
+
+
+@pytest.mark.parametrize("wl", [3, 4])
+def test_kv_one_buffer_two_groups(tq, wl):
+    """K and V of a layer in one [2, T, H, D] buffer with one global scale per
+    tensor (G = 2), as the benchmark runs the KV workloads; windows straddle
+    the K/V boundary."""
+    (_, shape), _ = synth.tensor_specs(wl)
+    K, Ky = synth.make_pair(wl, 0, shape, DEV)
+    V, Vy = synth.make_pair(wl, 1, shape, DEV)
+    X, Y = torch.stack([K, V]), torch.stack([Ky, Vy])
+    del K, Ky, V, Vy
+    nblk = X.numel() // 16
+    half = nblk // 2
+    wins = blocks_of(nblk, [(0, 400), (half - 300, half + 300), (nblk - 400, nblk)])
+    for k in synth.WORKLOADS[wl].ks:
+        c = Checker(tq, X, Y, k, 2)
+        c.run_gpu(out_f32=False)
+        c.check(wins)
