@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     p.add_argument("--k", type=int, default=2, choices=[1, 2], help="guidance bits of the compact stream")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-transport", action="store_true", help="skip the guidance-transport measurements")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
     p.add_argument("--separate-kv", action="store_true",
                    help="K and V as two tensors (G = 1 each) instead of one [2, T, H, D] buffer with G = 2")
@@ -396,7 +397,7 @@ def main():
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
-    transport = transport_stats(tq, graphs, sets, bufs, ns, Gs, min(K, 20), k)
+    transport = None if args.no_transport else transport_stats(tq, graphs, sets, bufs, ns, Gs, min(K, 20), k)
 
     cpu = None
     if not args.no_cpu:
