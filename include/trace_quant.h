@@ -41,7 +41,9 @@
  * Common rules for every entry point:
  *   - pointers are device pointers unless stated; the caller owns every
  *     buffer; the library never allocates device memory and keeps no state
- *     beyond a read-only kernel table; calls are thread-safe;
+ *     beyond a read-only kernel table and a host-side cache of device
+ *     attributes (compute units, LDS size, clock rate); calls are
+ *     thread-safe;
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns at once; outputs are valid once the stream has
  *     reached that point;
@@ -72,7 +74,9 @@ typedef enum {
     TRACE_E_HIP = -6,       /* the HIP runtime reported an error */
     TRACE_E_NONFINITE = -7, /* (device status word) an input was inf/NaN */
     TRACE_E_FORMAT = -8,    /* a guidance record fails its header or hash check */
-    TRACE_E_IO = -9         /* a file could not be opened, written or read */
+    TRACE_E_IO = -9,        /* a file could not be opened, written or read */
+    TRACE_E_BARRIER = -10   /* (device status word) the one-pass rollout's workgroups
+                               were not all resident at once; outputs undefined */
 } trace_status;
 
 typedef enum { TRACE_OUT_BF16 = 0, TRACE_OUT_F32 = 1 } trace_out_dtype;
@@ -103,6 +107,32 @@ int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_d
  * guidance: u8[trace_guidance_bytes(n, k)] or NULL (no guidance written). */
 int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, int k,
                         uint8_t *codes, uint8_t *scales, uint8_t *guidance, void *stream);
+
+/* Bytes of the work buffer of trace_quant_rollout_onepass: 4352 + 4 G,
+ * rounded up to a multiple of 256 (0 if G < 1). */
+size_t trace_onepass_work_bytes(int G);
+
+/* One-pass rollout: the results of trace_amax followed by trace_quant_rollout
+ * (bit for bit), from one read of y where it fits on chip.  The global scale
+ * needs the whole group before any block can be quantised ("Why Does FP4
+ * Rollout 'Break' RL Training?": both sides share the global scale); instead
+ * of reading y twice, one workgroup per compute unit keeps its share in VGPRs
+ * and LDS (about 116 MiB of bf16 over 256 CUs), meets the others at a
+ * grid-wide barrier once every group maximum is folded, and quantises from
+ * chip; the part that does not fit is read a second time.
+ * y_bf16: bf16[n]; g_out: f32[G], written; k, codes, scales, guidance: as
+ * trace_quant_rollout.  work: device buffer of trace_onepass_work_bytes(G)
+ * bytes, 16-byte aligned, owned by the caller; the call clears it itself (a
+ * fill kernel, so the call can be captured in a graph); calls that share a
+ * work buffer must be ordered on one stream.  max_workgroups: 0 = one per
+ * compute unit; a smaller cap leaves compute units to concurrent work but
+ * keeps less on chip.  status_dev: nullable int*, as trace_amax's
+ * (TRACE_E_NONFINITE), and TRACE_E_BARRIER if the workgroups were not all
+ * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s); the
+ * outputs are then undefined.  Enqueues two kernels (clear, one-pass). */
+int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
+                                int *status_dev, void *stream);
 
 /* Guidance stream from existing codes and scales (for example an FP4 KV cache
  * written elsewhere); same layout as trace_quant_rollout's.  "TRACE Core

@@ -35,6 +35,7 @@
 #include <bit>
 #include <cfloat>
 #include <cstdint>
+#include <mutex>
 
 #include "trace_quant.h"
 
@@ -203,21 +204,29 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 
 // E4M3 (OCP "FN") encode of t >= 0: nearest, ties to even, saturating at 448,
 // subnormals kept.
+// Both candidates are kept in registers before the select (an empty asm
+// that reads them), so the compiler cannot sink either into a branch: the
+// per-block code stays one basic block and tiles can be interleaved.
+__device__ __forceinline__ void keep(uint32_t a, uint32_t b) { asm volatile("" ::"v"(a), "v"(b)); }
+
+// All cases are computed and one is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float t)
 {
-    if (t >= 448.0f)
-        return 0x7eu;
-    if (t < 0.015625f)                                   // below 2^-6: step 2^-9
-        return (uint32_t)__builtin_rintf(t * 512.0f);     // exact scaling, RNE
+    uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f); // below 2^-6: step 2^-9 (exact scaling, RNE)
     uint32_t u = as_u(t);
     uint32_t r = u + 0x7ffffu + ((u >> 20) & 1u);        // RNE to 3 mantissa bits
-    return (r >> 20) - (120u << 3);                      // rebias 127 -> 7
+    uint32_t nrm = (r >> 20) - (120u << 3);              // rebias 127 -> 7
+    keep(sub, nrm);
+    return t >= 448.0f ? 0x7eu : (t < 0.015625f ? sub : nrm);
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c)
 {
     uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    return e ? as_f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    uint32_t nrm = ((e + 120u) << 23) | (m << 20);
+    uint32_t sub = as_u((float)m * 0.001953125f);
+    keep(nrm, sub);
+    return as_f(e ? nrm : sub);
 }
 
 // Reciprocal of the combined scale c = s * g: 0 when c == 0, FLT_MAX when
@@ -225,18 +234,15 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c)
 __device__ __forceinline__ float inv_combined(float s, float g)
 {
     float c = s * g;
-    if (!(c > 0.0f))
-        return 0.0f;
-    return fminf(1.0f / c, FLT_MAX);
+    float inv = fminf(1.0f / c, FLT_MAX);                // 1 / 0 = inf is discarded below
+    return c > 0.0f ? inv : 0.0f;
 }
 
 // Block scale from the block amax and g (t = 0 when g == 0).
 __device__ __forceinline__ uint32_t block_scale(float ab, float g)
 {
-    float t = 0.0f;
-    if (g > 0.0f)
-        t = ab / (6.0f * g);
-    return e4m3_encode(t);
+    float q = ab / (6.0f * g);                           // inf or NaN when g == 0, discarded
+    return e4m3_encode(g > 0.0f ? q : 0.0f);
 }
 
 // Unsigned division by an invariant d (Granlund & Montgomery 1994, Fig. 4.1).
@@ -455,11 +461,13 @@ __device__ __forceinline__ void load_table(Entry *lds, const Entry *src)
     __syncthreads();
 }
 
-// Zero the pad between the scale plane and the bit plane of a guidance stream.
+// Zero the pad between the scale plane and the bit plane of a guidance stream
+// (workgroup 0 of a launch of T threads per workgroup).
+template <int T>
 __device__ __forceinline__ void zero_pad(uint8_t *gd, uint32_t begin, uint32_t end)
 {
     if (blockIdx.x == 0)
-        for (uint32_t p = begin + threadIdx.x; p < end; p += kThreads)
+        for (uint32_t p = begin + threadIdx.x; p < end; p += T)
             gd[p] = 0;
 }
 
@@ -480,6 +488,23 @@ __device__ __forceinline__ void store_bits(uint8_t *gd_bits, uint32_t c, uint32_
 // Kernels
 // ---------------------------------------------------------------------------
 
+// max |x| over the finite elements of a chunk (bf16 magnitude bits); an inf
+// or NaN is left out and flagged in *status (when given).
+__device__ __forceinline__ uint32_t chunk_amax_finite(const Chunk &x, int *status)
+{
+    uint32_t m = chunk_amax_bits(x);
+    if (m >= 0x7f80u) {                                    // rare: an inf or NaN in the chunk
+        m = 0;
+        for (int i = 0; i < 4; ++i) {
+            uint32_t lo = x.w[i] & 0x7fffu, hi = (x.w[i] >> 16) & 0x7fffu;
+            m = max(m, max(lo < 0x7f80u ? lo : 0u, hi < 0x7f80u ? hi : 0u));
+        }
+        if (status)
+            *status = TRACE_E_NONFINITE;
+    }
+    return m;
+}
+
 __global__ void k_amax_clear(uint32_t *g_bits, int G)
 {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -489,6 +514,10 @@ __global__ void k_amax_clear(uint32_t *g_bits, int G)
 
 // Fold the workgroup's running max and raise the group's word with one atomic
 // max, skipped when the word already holds a value at least as large.
+// kPerformed: use the returning form of the atomic and wait for it, so the
+// maximum has been performed at the device's coherence point when the
+// function returns (the one-pass kernel's barrier arrival depends on it).
+template <int T = kAmaxThreads, bool kPerformed = false>
 __device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint32_t *word)
 {
     uint32_t m = run;
@@ -499,11 +528,17 @@ __device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint3
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t b = 0;
-        for (int i = 0; i < kAmaxThreads / 64; ++i)
+        for (int i = 0; i < T / 64; ++i)
             b = max(b, wmax[i]);
         b <<= 16;
-        if (b > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            atomicMax(word, b);
+        if (b > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            if (kPerformed) {
+                wmax[0] = __hip_atomic_fetch_max(word, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+            } else {
+                atomicMax(word, b);
+            }
+        }
     }
     __syncthreads();
 }
@@ -538,21 +573,9 @@ __global__ void __launch_bounds__(kAmaxThreads)
             if (ok[u])
                 b[u] = load_chunk(x, base + j);
         }
-        for (int u = 0; u < kAmaxUnroll; ++u) {
-            if (!ok[u])
-                continue;
-            uint32_t m = chunk_amax_bits(b[u]);
-            if (m >= 0x7f80u) {                            // rare: an inf or NaN in the chunk
-                m = 0;
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t lo = b[u].w[i] & 0x7fffu, hi = (b[u].w[i] >> 16) & 0x7fffu;
-                    m = max(m, max(lo < 0x7f80u ? lo : 0u, hi < 0x7f80u ? hi : 0u));
-                }
-                if (status)
-                    *status = TRACE_E_NONFINITE;
-            }
-            run = max(run, m);
-        }
+        for (int u = 0; u < kAmaxUnroll; ++u)
+            if (ok[u])
+                run = max(run, chunk_amax_finite(b[u], status));
     }
     if (cur != 0xffffffffu)
         amax_publish(run, wmax, g_bits + cur);
@@ -565,6 +588,53 @@ __global__ void k_amax_finalize(float *g, int G)
         g[i] = g[i] / 2688.0f;                   // g[i] holds the amax bits
 }
 
+// RTN codes, scale bytes and (with gd_scales) guidance bits of one lane's U
+// chunks cs[u], which hold x[u]; chunks at or past `lim` are outside the
+// tensor (or group) and are skipped (both lanes of a pair always agree).
+// gg[u] is the global scale of chunk u.
+template <int K, int U>
+__device__ __forceinline__ void quant_lane(const Chunk (&xc)[U], const uint32_t (&cs)[U], uint32_t lim,
+                                           const float (&gg)[U], uint32_t *__restrict__ codes,
+                                           uint8_t *__restrict__ scales, uint8_t *__restrict__ gd_scales,
+                                           uint8_t *__restrict__ gd_bits)
+{
+    uint32_t sc[U];
+    float inv[U];
+    if constexpr (TRACE_PAIR_SPLIT && U == 2) {
+        PairScales ps = pair_scales_from_amax(pair_max(chunk_amax_bits(xc[0])), pair_max(chunk_amax_bits(xc[1])),
+                                              gg[0], gg[1]);
+        for (int u = 0; u < U; ++u) {
+            sc[u] = ps.sc[u];
+            inv[u] = ps.inv[u];
+        }
+        int mine = threadIdx.x & 1;                // each lane writes the scale byte of the block it derived
+        uint32_t c = cs[mine];
+        if (c < lim) {
+            scales[c >> 1] = (uint8_t)sc[mine];
+            if (gd_scales)
+                gd_scales[c >> 1] = (uint8_t)sc[mine];
+        }
+    } else {
+        for (int u = 0; u < U; ++u) {
+            sc[u] = block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg[u]);
+            inv[u] = inv_combined(e4m3_decode(sc[u]), gg[u]);
+            if (cs[u] < lim && (cs[u] & 1u) == 0) {
+                scales[cs[u] >> 1] = (uint8_t)sc[u];
+                if (gd_scales)
+                    gd_scales[cs[u] >> 1] = (uint8_t)sc[u];
+            }
+        }
+    }
+    for (int u = 0; u < U; ++u) {
+        if (cs[u] >= lim)
+            continue;
+        uint32_t cw = rtn8(xc[u], inv[u]);
+        st_stream(cw, codes + cs[u]);
+        if (gd_scales)
+            store_bits<K>(gd_bits, cs[u], cw);
+    }
+}
+
 // Rollout: RTN codes, scale bytes, and (optionally) the guidance stream.
 template <int K, bool kOneGroup>
 __global__ void __launch_bounds__(kThreads)
@@ -574,7 +644,7 @@ __global__ void __launch_bounds__(kThreads)
                     uint32_t pad_end)
 {
     if (gd_scales)
-        zero_pad(gd_scales, pad_begin, pad_end);
+        zero_pad<kThreads>(gd_scales, pad_begin, pad_end);
     uint32_t ntiles = (nchunk + kTile - 1) / kTile;
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         Chunk xc[kUnroll];
@@ -585,48 +655,422 @@ __global__ void __launch_bounds__(kThreads)
         }
         if (cs[0] >= nchunk)                       // later chunks of this lane are further out
             continue;
-        uint32_t sc[kUnroll];
-        float inv[kUnroll];
         float gg[kUnroll];
         for (int u = 0; u < kUnroll; ++u)
             gg[u] = group_scale<kOneGroup>(g, cs[u] >> 1, dm, last_group);
-#if TRACE_PAIR_SPLIT
-        PairScales ps = pair_scales_from_amax(pair_max(chunk_amax_bits(xc[0])), pair_max(chunk_amax_bits(xc[1])),
-                                              gg[0], gg[1]);
-        for (int u = 0; u < kUnroll; ++u) {
-            sc[u] = ps.sc[u];
-            inv[u] = ps.inv[u];
-        }
-        {   // each lane writes the scale byte of the block it derived
-            int mine = threadIdx.x & 1;
-            uint32_t c = cs[mine];
-            if (c < nchunk) {
-                scales[c >> 1] = (uint8_t)sc[mine];
-                if (gd_scales)
-                    gd_scales[c >> 1] = (uint8_t)sc[mine];
-            }
-        }
-#else
-        for (int u = 0; u < kUnroll; ++u) {
-            sc[u] = block_scale(as_f(pair_max(chunk_amax_bits(xc[u])) << 16), gg[u]);
-            inv[u] = inv_combined(e4m3_decode(sc[u]), gg[u]);
-            if (cs[u] < nchunk && (cs[u] & 1u) == 0) {
-                scales[cs[u] >> 1] = (uint8_t)sc[u];
-                if (gd_scales)
-                    gd_scales[cs[u] >> 1] = (uint8_t)sc[u];
-            }
-        }
+        quant_lane<K>(xc, cs, nchunk, gg, codes, scales, gd_scales, gd_bits);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One-pass rollout: group amax, then quantisation, in one kernel.
+//
+// The two-kernel rollout reads y twice (amax, then quantise), because no block
+// can be quantised before its group's global scale is known.  Here every
+// workgroup (one per compute unit, all resident at once) reads its share of y
+// once, keeps as much of it as fits on chip (kOpRegTiles tiles in VGPRs, a
+// runtime number in LDS), folds its maximum into the group's word, and waits
+// at a grid-wide barrier; after it, the kept tiles are quantised from
+// registers and LDS, and only the tiles that did not fit are read again.
+// 512 threads per workgroup: two waves per SIMD leave each lane 256 VGPRs, of
+// which 160 hold tiles.  Work items are (group, tile) pairs, so a tile never
+// straddles two groups; workgroup w takes a contiguous run of items: first the
+// ones it reads twice, then the LDS ones, then the register ones.  Within a
+// tile each lane owns one 16-element block (two adjacent chunks), so the
+// block maximum needs no exchange between lanes and each output plane takes
+// one store per lane.
+// ---------------------------------------------------------------------------
+#ifndef TRACE_OP_REG_TILES
+#define TRACE_OP_REG_TILES 24
 #endif
-        for (int u = 0; u < kUnroll; ++u) {
-            uint32_t c = cs[u];
-            if (c >= nchunk)
-                continue;
-            uint32_t cw = rtn8(xc[u], inv[u]);
-            st_stream(cw, codes + c);
-            if (gd_scales)
-                store_bits<K>(gd_bits, c, cw);
+#ifndef TRACE_OP_THREADS
+#define TRACE_OP_THREADS 512
+#endif
+constexpr int kOpThreads = TRACE_OP_THREADS;
+constexpr int kOpTile = 2 * kOpThreads;            // chunks per tile (16 KiB of bf16)
+constexpr int kOpRegTiles = TRACE_OP_REG_TILES;
+constexpr int kOpStream = 8;                       // tiles in flight per lane when streaming
+// Work buffer (words): arrival counters of 16 subgroups of workgroups and
+// one top counter, each on its own 256-byte line (a same-address atomic costs
+// about 30 ns on MI355X, so 256 arrivals on one word serialise for ~8 us;
+// two levels of 16 take ~1 us), then the group amax bits.
+#ifndef TRACE_OP_LINE_WORDS
+#define TRACE_OP_LINE_WORDS 64
+#endif
+constexpr uint32_t kOpLine = TRACE_OP_LINE_WORDS;
+constexpr uint32_t kOpSubgroups = 16;
+constexpr uint32_t kOpTopWord = kOpSubgroups * kOpLine;
+constexpr uint32_t kOpAccWord = (kOpSubgroups + 1) * kOpLine;
+constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
+
+struct OnePass {
+    const u32x4 *y;
+    uint32_t cpg;           // chunks per group
+    uint32_t tpg;           // tiles per group
+    uint32_t items;         // G * tpg
+    uint32_t G;
+    uint32_t lds_tiles;     // tiles a workgroup keeps in LDS
+    uint32_t pad_begin, pad_end;
+    uint64_t wait_ticks;    // barrier time limit in wall-clock ticks
+    uint32_t *work;
+    float *g_out;
+    int *status;
+    uint32_t *codes;
+    uint8_t *scales, *gd_scales, *gd_bits;
+};
+
+// Where the chunks of item it lie (all uniform): chunk u of thread t is
+// first + u * T + t, so each load is 16 bytes per lane, contiguous across the
+// wave; valid while u * T + t < count (the group's last tile may be short;
+// count is even).
+struct Item {
+    uint32_t grp, first, count;
+};
+
+template <bool kOneGroup>
+__device__ __forceinline__ Item item_at(const OnePass &a, uint32_t it)
+{
+    uint32_t grp = kOneGroup ? 0u : it / a.tpg;
+    uint32_t tile = it - grp * a.tpg;
+    uint32_t off = tile * kOpTile;
+    return Item{grp, grp * a.cpg + off, min(a.cpg - off, (uint32_t)kOpTile)};
+}
+
+// Buffer descriptor over an item's chunks (gfx9 raw buffer, stride 0): loads
+// past `count` chunks return zeros, which leave a maximum unchanged and are
+// never stored; an item that is not live gets no records at all.  So every
+// load of a batch is issued without a branch and stays in flight together,
+// and the per-lane offset is a 32-bit register instead of a 64-bit address.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rsrc(const OnePass &a, const Item &w, bool live)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(a.y + (live ? w.first : 0u)), (short)0,
+                                             live ? (int)(w.count * 16u) : 0, 0x00020000);
+}
+
+__device__ __forceinline__ void load_item(const OnePass &a, const Item &w, bool live, Chunk (&x)[2])
+{
+    __amdgpu_buffer_rsrc_t r = item_rsrc(a, w, live);
+    for (int u = 0; u < 2; ++u) {
+        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (u * kOpThreads + threadIdx.x) * 16u, 0,
+                                                        TRACE_NT_LOAD ? 2 : 0);
+        x[u] = Chunk{{v.x, v.y, v.z, v.w}};
+    }
+}
+
+// Copy this lane's two chunks of an item straight into LDS slot j
+// (global_load_lds, 16 bytes: lane i of a wave lands at the wave's base +
+// 16 i, so chunk u * T + t sits at (2 j + u) * T + t).  Lanes past the
+// item's end load nothing; their slots are masked or never stored.
+__device__ __forceinline__ void load_item_to_lds(const OnePass &a, const Item &w, u32x4 *lds, uint32_t j)
+{
+    uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int u = 0; u < 2; ++u) {
+        uint32_t o = u * kOpThreads + threadIdx.x;
+        u32x4 *dst = lds + ((2 * j + u) * kOpThreads + wave * 64);
+        if (o < w.count)
+            __builtin_amdgcn_global_load_lds(a.y + w.first + o, (__attribute__((address_space(3))) void *)dst, 16, 0,
+                                             0);
+    }
+}
+
+// This lane's own two chunks of LDS slot j (chunks past the end as zeros).
+__device__ __forceinline__ void read_item_from_lds(const u32x4 *lds, const Item &w, uint32_t j, Chunk (&x)[2])
+{
+    for (int u = 0; u < 2; ++u) {
+        u32x4 v = lds[(2 * j + u) * kOpThreads + threadIdx.x];
+        x[u] = u * kOpThreads + threadIdx.x < w.count ? Chunk{{v.x, v.y, v.z, v.w}} : Chunk{{0u, 0u, 0u, 0u}};
+    }
+}
+
+// One whole 16-element block per lane.  Lanes 2m and 2m + 1 hold chunks
+// (2m, T + 2m) and (2m + 1, T + 2m + 1); one DPP swap per word hands the
+// even lane chunk 2m + 1 and the odd lane chunk T + 2m, so the even lane
+// owns block m of the item and the odd lane block T/2 + m.
+struct Blk {
+    Chunk lo, hi;
+};
+
+__device__ __forceinline__ uint32_t block_of_lane()
+{
+    uint32_t t = threadIdx.x;
+    return (t & 1u) ? kOpThreads / 2 + (t >> 1) : (t >> 1);
+}
+
+__device__ __forceinline__ Blk to_block(const Chunk (&x)[2])
+{
+    bool odd = threadIdx.x & 1u;
+    Blk b;
+    for (int i = 0; i < 4; ++i) {
+        uint32_t recv = pair_swap(odd ? x[0].w[i] : x[1].w[i]);
+        b.lo.w[i] = odd ? recv : x[0].w[i];
+        b.hi.w[i] = odd ? x[1].w[i] : recv;
+    }
+    return b;
+}
+
+// The same block straight from LDS slot j (no exchange needed: a lane may
+// read its neighbour's slot).  Blocks past the item's end hold stale data
+// and are never stored.
+__device__ __forceinline__ Blk block_from_lds(const u32x4 *lds, uint32_t j)
+{
+    uint32_t t = threadIdx.x, odd = t & 1u;
+    const u32x4 *p = lds + (2 * j + odd) * kOpThreads + t - odd;
+    u32x4 a = p[0], b = p[1];
+    return Blk{Chunk{{a.x, a.y, a.z, a.w}}, Chunk{{b.x, b.y, b.z, b.w}}};
+}
+
+__device__ __forceinline__ uint32_t block_amax_bits(const Blk &b)
+{
+    return max(chunk_amax_bits(b.lo), chunk_amax_bits(b.hi));
+}
+
+__device__ __forceinline__ uint32_t group_amax_bits(const OnePass &a, uint32_t grp)
+{
+    return __hip_atomic_load(a.work + kOpAccWord + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Buffer descriptor over `bytes` bytes at p (gfx9 raw buffer, stride 0);
+// accesses past the end are dropped (stores) or read as zero (loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Output descriptors.  Span form (kSpan): one descriptor per output over this
+// workgroup's whole run of chunks [c0, c0 + n), fixed for the whole phase; a
+// tile's stores add its offset in the run to the lane offset.  Valid when no
+// tile inside the run is short of kOpTile chunks except the run's last (one
+// group, or groups of whole tiles), since a short tile's missing chunks would
+// otherwise alias the next tile's.  Item form: one descriptor per output over
+// the item's own slice, for groups whose last tile is short.  Items that are
+// not live get descriptors with no records.
+struct Outs {
+    __amdgpu_buffer_rsrc_t codes, scales, gds, bits;
+    uint32_t c0;               // first chunk covered
+};
+
+template <int K>
+__device__ __forceinline__ Outs outs_over(const OnePass &a, uint32_t c0, uint32_t n)
+{
+    const bool gd = a.gd_scales != nullptr;
+    return Outs{span_rsrc(a.codes + c0, n * 4u), span_rsrc(a.scales + c0 / 2, n / 2),
+                span_rsrc(gd ? a.gd_scales + c0 / 2 : a.scales, gd ? n / 2 : 0u),
+                span_rsrc(gd ? a.gd_bits + (size_t)c0 * K : a.scales, gd ? n * K : 0u), c0};
+}
+
+// Codes, scale byte and guidance bits of this lane's block of one item (raw
+// amax bits ab): one store per plane per lane (8 code bytes, 2k bit-plane
+// bytes, one byte in each scale plane), with no branch.
+template <int K>
+__device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv)
+{
+    const uint32_t cb = w.first - o.c0 + 2 * block_of_lane();   // the block's first chunk, in o's span
+    const uint32_t sc = block_scale(as_f(ab << 16), gv);
+    const float inv = inv_combined(e4m3_decode(sc), gv);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.scales, cb / 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.gds, cb / 2, 0, 0);
+    const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.codes, cb * 4u, 0, TRACE_NT_STORE ? 2 : 0);
+    if (K == 4)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.bits, cb * 4u, 0, 0);
+    else if (K == 2)
+        __builtin_amdgcn_raw_buffer_store_b32(compact_k2(c0) | (compact_k2(c1) << 16), o.bits, cb * 2u, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(compact_k1(c0) | (compact_k1(c1) << 8)), o.bits, cb, 0, 0);
+}
+
+// kSpan: output descriptors over the workgroup's whole run (see Outs).
+template <int K, bool kOneGroup, bool kSpan>
+__global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
+{
+    extern __shared__ u32x4 lds_tiles[];           // a.lds_tiles * 2 * kOpThreads chunks
+    __shared__ uint32_t wmax[kOpThreads / 64];
+    __shared__ int passed;
+    __shared__ float gslot[kOpGroupSlots];
+
+    const uint32_t P = gridDim.x;
+    const uint32_t i0 = (uint32_t)((uint64_t)a.items * blockIdx.x / P);
+    const uint32_t cnt = (uint32_t)((uint64_t)a.items * (blockIdx.x + 1) / P) - i0;
+    const uint32_t nreg = min(cnt, (uint32_t)kOpRegTiles);
+    const uint32_t nlds = min(cnt - nreg, a.lds_tiles);
+    const uint32_t nstr = cnt - nreg - nlds;
+    const uint32_t i_lds = i0 + nstr, i_reg = i_lds + nlds;
+    uint32_t *acc = a.work + kOpAccWord;
+
+    // ---- phase 1: read everything once, fold the group maxima ------------
+    // The LDS tiles go first, straight from memory into LDS (no VGPRs, and
+    // they stay in flight behind the rest); then the tiles read twice, a
+    // batch at a time; then the register tiles, all at once.
+    for (uint32_t j = 0; j < nlds; ++j)
+        load_item_to_lds(a, item_at<kOneGroup>(a, i_lds + j), lds_tiles, j);
+    uint32_t run = 0;
+    uint32_t cur = kOneGroup ? 0u : i0 / a.tpg;
+    auto fold = [&](uint32_t grp, uint32_t m) {
+        if (!kOneGroup && grp != cur) {            // uniform: all lanes walk the same items
+            amax_publish<kOpThreads, true>(run, wmax, acc + cur);
+            run = 0;
+            cur = grp;
+        }
+        run = max(run, m);
+    };
+    auto chunk_pair_max = [&](const Chunk (&x)[2]) {
+        return max(chunk_amax_finite(x[0], a.status), chunk_amax_finite(x[1], a.status));
+    };
+    for (uint32_t j = 0; j < nstr; j += kOpStream) {
+        Chunk x[kOpStream][2];
+        Item w[kOpStream];
+        for (int q = 0; q < kOpStream; ++q) {
+            w[q] = item_at<kOneGroup>(a, i0 + j + q);
+            load_item(a, w[q], j + q < nstr, x[q]);
+        }
+        for (int q = 0; q < kOpStream; ++q)
+            if (j + q < nstr)
+                fold(w[q].grp, chunk_pair_max(x[q]));
+    }
+    // Register tiles: loaded coalesced, then regrouped into one block per lane
+    // and the block's raw amax kept, while this phase waits on memory anyway.
+    Blk hr[kOpRegTiles];
+    uint32_t hab[kOpRegTiles];
+#pragma unroll
+    for (int h = 0; h < kOpRegTiles; ++h) {
+        Chunk x[2];
+        load_item(a, item_at<kOneGroup>(a, i_reg + h), (uint32_t)h < nreg, x);
+        hr[h].lo = x[0];
+        hr[h].hi = x[1];
+    }
+    __builtin_amdgcn_s_waitcnt(0);                 // the LDS copies have landed (this wave's own)
+    for (uint32_t j = 0; j < nlds; ++j) {
+        Item w = item_at<kOneGroup>(a, i_lds + j);
+        Chunk x[2];
+        read_item_from_lds(lds_tiles, w, j, x);
+        fold(w.grp, chunk_pair_max(x));
+    }
+#pragma unroll
+    for (int h = 0; h < kOpRegTiles; ++h) {
+        Chunk x[2] = {hr[h].lo, hr[h].hi};
+        hr[h] = to_block(x);
+        hab[h] = block_amax_bits(hr[h]);
+        if ((uint32_t)h < nreg) {
+            uint32_t m = hab[h] < 0x7f80u ? hab[h]
+                                          : max(chunk_amax_finite(hr[h].lo, a.status), chunk_amax_finite(hr[h].hi, a.status));
+            fold(item_at<kOneGroup>(a, i_reg + h).grp, m);
         }
     }
+    if (cnt > 0)
+        amax_publish<kOpThreads, true>(run, wmax, acc + cur);
+
+    // ---- grid barrier ------------------------------------------------------
+    // Bounded: a launch whose workgroups are not all resident gives up after
+    // wait_ticks and reports TRACE_E_BARRIER.  The arrival and the spin are
+    // device-scope atomics on one word; every maximum this workgroup published
+    // has been performed (returning atomic, waited for) before it arrives, and
+    // the group maxima are read back below with device-scope atomic loads.
+    // Nothing else crosses workgroups before the outputs, so no cache-wide
+    // acquire or release fence is needed (on MI355X each is a pass over the
+    // L2 of every XCD, measured at over 10 us for this kernel).
+    // Arrival is a two-level tree: workgroup b counts into subgroup b % 16;
+    // the last member of a subgroup (all members' maxima performed before
+    // their counts) counts into the top word, which everyone watches.
+    if (threadIdx.x == 0) {
+        const uint32_t sub = blockIdx.x % kOpSubgroups;
+        const uint32_t members = (P - sub + kOpSubgroups - 1) / kOpSubgroups;
+        const uint32_t nsub = min(P, kOpSubgroups);
+        uint32_t *top = a.work + kOpTopWord;
+        if (__hip_atomic_fetch_add(a.work + sub * kOpLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            members - 1)
+            __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t t0 = (uint64_t)wall_clock64();
+        int ok = 1;
+        while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nsub) {
+            __builtin_amdgcn_s_sleep(8);
+            if ((uint64_t)wall_clock64() - t0 > a.wait_ticks) {
+                ok = 0;
+                break;
+            }
+        }
+        passed = ok;
+    }
+    __syncthreads();
+    if (!passed) {
+        if (threadIdx.x == 0 && a.status)
+            *a.status = TRACE_E_BARRIER;
+        return;
+    }
+    // Global scales of the groups this workgroup touches, into LDS (groups
+    // past kOpGroupSlots, possible only for groups of a few tiles, are read
+    // per item by one lane of each wave).
+    const uint32_t g_first = kOneGroup ? 0u : i0 / a.tpg;
+    const uint32_t g_count = kOneGroup ? 1u : min((i0 + cnt - 1) / a.tpg - g_first + 1, (uint32_t)kOpGroupSlots);
+    for (uint32_t i = threadIdx.x; i < g_count; i += kOpThreads)
+        gslot[i] = as_f(group_amax_bits(a, g_first + i)) / 2688.0f;
+    __syncthreads();
+
+    // ---- phase 2: quantise ------------------------------------------------
+    // Item positions are recomputed from a copy the compiler cannot see
+    // through, so the scalar values of phase 1 are not kept alive (in spilled
+    // SGPRs) across the barrier.
+    uint32_t p2_reg = i_reg, p2_lds = i_lds;
+    asm volatile("" : "+s"(p2_reg), "+s"(p2_lds));
+    if (blockIdx.x == 0) {
+        for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
+            a.g_out[i] = as_f(group_amax_bits(a, i)) / 2688.0f;
+        if (a.gd_scales)
+            zero_pad<kOpThreads>(a.gd_scales, a.pad_begin, a.pad_end);
+    }
+    auto gscale = [&](uint32_t grp) {
+        if (kOneGroup)
+            return gslot[0];
+        uint32_t i = grp - g_first;
+        if (i < (uint32_t)kOpGroupSlots)
+            return gslot[i];
+        uint32_t bits = 0;
+        if (__lane_id() == 0)
+            bits = group_amax_bits(a, grp);
+        return as_f(__builtin_amdgcn_readfirstlane(bits)) / 2688.0f;
+    };
+    // register tiles: straight-line code (tiles past nreg store nothing)
+    // the run of chunks this workgroup owns (items are consecutive, and with
+    // kSpan only the run's last item can be short)
+    const Item w_first = item_at<kOneGroup>(a, i0), w_last = item_at<kOneGroup>(a, i0 + cnt - 1);
+    const Outs span = outs_over<K>(a, w_first.first, w_last.first + w_last.count - w_first.first);
+    const Outs none = outs_over<K>(a, 0u, 0u);      // no records: every store dropped
+    auto outs_for = [&](const Item &w, bool live) {
+        // An item that is not live stores nothing wherever it lies (a batch of
+        // read-twice items can run past its last one into the LDS items).
+        if (!live)
+            return none;
+        return kSpan ? span : outs_over<K>(a, w.first, w.count);
+    };
+#pragma unroll
+    for (int h = 0; h < kOpRegTiles; ++h) {
+        Item w = item_at<kOneGroup>(a, p2_reg + h);
+        bool live = p2_reg + h < i0 + cnt;
+        quant_block<K>(outs_for(w, live), w, hr[h], hab[h], live ? gscale(w.grp) : 0.0f);
+    }
+    for (uint32_t j = 0; j < nlds; ++j) {
+        Item w = item_at<kOneGroup>(a, p2_lds + j);
+        Blk b = block_from_lds(lds_tiles, j);
+        quant_block<K>(outs_for(w, true), w, b, block_amax_bits(b), gscale(w.grp));
+    }
+    for (uint32_t j = 0; j < nstr; j += kOpStream) {
+        Chunk x[kOpStream][2];
+        Item w[kOpStream];
+        for (int q = 0; q < kOpStream; ++q) {
+            w[q] = item_at<kOneGroup>(a, i0 + j + q);
+            load_item(a, w[q], j + q < nstr, x[q]);
+        }
+        for (int q = 0; q < kOpStream; ++q) {
+            bool live = j + q < nstr;
+            Blk b = to_block(x[q]);
+            quant_block<K>(outs_for(w[q], live), w[q], b, block_amax_bits(b), live ? gscale(w[q].grp) : 0.0f);
+        }
+    }
+}
+
+__global__ void k_onepass_clear(uint32_t *work, uint32_t words)
+{
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x)
+        work[i] = 0u;
 }
 
 // Guidance stream from codes + scales.  Each lane packs four chunks (two
@@ -638,7 +1082,7 @@ __global__ void __launch_bounds__(kThreads)
                     uint8_t *__restrict__ gd_scales, uint8_t *__restrict__ gd_bits, uint32_t pad_begin,
                     uint32_t pad_end)
 {
-    zero_pad(gd_scales, pad_begin, pad_end);
+    zero_pad<kThreads>(gd_scales, pad_begin, pad_end);
     uint32_t q = blockIdx.x * kThreads + threadIdx.x;     // quad of chunks
     uint32_t c = 4 * q;
     if (c + 4 <= nchunk) {
@@ -910,9 +1354,125 @@ int check_common(const void *x, int64_t n, int G, const float *g, void *y, int o
     return TRACE_OK;
 }
 
+// Device facts the one-pass launch depends on, queried once per device.
+struct OnePassDevice {
+    int cus = 0;               // compute units
+    int per_cu = 0;            // resident one-pass workgroups per compute unit
+    uint32_t lds_tiles = 0;    // tiles a workgroup keeps in LDS
+    int64_t clock_khz = 0;     // wall-clock rate
+};
+
+constexpr int kMaxDevices = 64;
+
+int onepass_device(OnePassDevice &out)
+{
+    static OnePassDevice cache[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TRACE_E_HIP;
+    std::call_once(once[dev], [dev] {
+        OnePassDevice d;
+        int lds = 0, khz = 0, per = 0;
+        if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+            return;
+        // static LDS of the kernel (under 1 KiB) sits below the dynamic tiles
+        d.lds_tiles = lds > 1024 ? (uint32_t)((lds - 1024) / (kOpTile * 16)) : 0u;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_quant_onepass<2, true, true>, kOpThreads,
+                                                         (size_t)d.lds_tiles * kOpTile * 16) != hipSuccess)
+            return;
+        d.per_cu = per;
+        d.clock_khz = khz;
+        cache[dev] = d;
+    });
+    (void)hipGetLastError();
+    out = cache[dev];
+    return out.cus > 0 && out.per_cu > 0 && out.clock_khz > 0 ? TRACE_OK : TRACE_E_HIP;
+}
+
+uint32_t onepass_work_words(int G) { return kOpAccWord + (uint32_t)G; }
+
 }  // namespace
 
 extern "C" {
+
+size_t trace_onepass_work_bytes(int G)
+{
+    if (G < 1)
+        return 0;
+    return ((size_t)onepass_work_words(G) * 4 + 255) / 256 * 256;
+}
+
+int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
+                                int *status_dev, void *stream)
+{
+    int rc = check_sizes(n, G);
+    if (rc)
+        return rc;
+    if (!y_bf16 || !g_out || !codes || !scales || !work)
+        return TRACE_E_NULL;
+    if (!aligned16(y_bf16) || !aligned16(g_out) || !aligned16(codes) || !aligned16(scales) ||
+        (guidance && !aligned16(guidance)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
+        return TRACE_E_ALIGN;
+    if (k != 1 && k != 2 && k != 4)
+        return TRACE_E_K;
+    if (max_workgroups < 0)
+        return TRACE_E_SIZE;
+    OnePassDevice d;
+    if ((rc = onepass_device(d)) != TRACE_OK)
+        return rc;
+    OnePass a;
+    uint32_t nchunk = (uint32_t)(n / 8);
+    a.y = (const u32x4 *)y_bf16;
+    a.cpg = nchunk / (uint32_t)G;
+    a.tpg = (a.cpg + kOpTile - 1) / kOpTile;
+    a.items = a.tpg * (uint32_t)G;                       // <= nchunk / 2 + G < 2^32
+    a.G = (uint32_t)G;
+    a.lds_tiles = d.lds_tiles;
+    a.pad_begin = (uint32_t)(n / 16);
+    a.pad_end = (uint32_t)bitplane_offset(n);
+    // the longest legitimate wait is one pass over y; allow 1 s plus y at 50 GB/s
+    double secs = 1.0 + (double)n * 2.0 / 5.0e10;
+    a.wait_ticks = (uint64_t)(secs * (double)d.clock_khz * 1000.0);
+    a.work = (uint32_t *)work;
+    a.g_out = g_out;
+    a.status = status_dev;
+    a.codes = (uint32_t *)codes;
+    a.scales = scales;
+    a.gd_scales = guidance;
+    a.gd_bits = guidance ? guidance + bitplane_offset(n) : nullptr;
+    int64_t grid = (int64_t)d.cus * d.per_cu;
+    if (max_workgroups > 0 && max_workgroups < grid)
+        grid = max_workgroups;
+    if (grid > (int64_t)a.items)
+        grid = a.items;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t words = onepass_work_words(G);
+    size_t lds = (size_t)a.lds_tiles * kOpTile * 16;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_onepass_clear, dim3((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024), dim3(256), 0,
+                       st, (uint32_t *)work, words);
+#define TRACE_OP(KK, ONE, SPAN) \
+    hipLaunchKernelGGL((k_quant_onepass<KK, ONE, SPAN>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
+    if (G == 1) {                                      // one group: only the tensor's last tile can be short
+        if (k == 1) TRACE_OP(1, true, true);
+        else if (k == 2) TRACE_OP(2, true, true);
+        else TRACE_OP(4, true, true);
+    } else if (a.cpg % kOpTile == 0) {                 // groups of whole tiles
+        if (k == 1) TRACE_OP(1, false, true);
+        else if (k == 2) TRACE_OP(2, false, true);
+        else TRACE_OP(4, false, true);
+    } else {
+        if (k == 1) TRACE_OP(1, false, false);
+        else if (k == 2) TRACE_OP(2, false, false);
+        else TRACE_OP(4, false, false);
+    }
+#undef TRACE_OP
+    return launched();
+}
 
 size_t trace_code_bytes(int64_t n) { return check_sizes(n, 1) ? 0 : (size_t)(n / 2); }
 
@@ -1081,10 +1641,11 @@ const char *trace_status_str(int status)
     case TRACE_E_NONFINITE: return "an input was inf or NaN";
     case TRACE_E_FORMAT: return "guidance record fails its header or hash check";
     case TRACE_E_IO: return "file could not be opened, written or read";
+    case TRACE_E_BARRIER: return "one-pass rollout: workgroups were not all resident (grid barrier timed out)";
     default: return "unknown status";
     }
 }
 
-int trace_version(void) { return 300; }
+int trace_version(void) { return 400; }
 
 }  // extern "C"

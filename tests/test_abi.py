@@ -51,6 +51,9 @@ def test_sizes(tq):
     assert tq.code_bytes(17) == 0 and tq.code_bytes(0) == 0
     assert tq.version() >= 100
     assert tq.lib.trace_status_str(-7).decode().startswith("an input")
+    assert tq.onepass_work_bytes(1) == 4608 and tq.onepass_work_bytes(64) == 4608
+    assert tq.onepass_work_bytes(65) == 4864 and tq.onepass_work_bytes(0) == 0
+    assert "barrier" in tq.lib.trace_status_str(-10).decode()
 
 
 def test_argument_errors_before_any_hip_call(tq):
@@ -82,6 +85,17 @@ def test_argument_errors_before_any_hip_call(tq):
     assert L.trace_fakequant_guided(A, n, 1, A, A, 4, A, 0, None, None) == E_K
     assert L.trace_fakequant_guided(A, n, 1, A, A, 2, A, 7, None, None) == E_DTYPE
     assert L.trace_fakequant_rtn(A, n, 1, A, None, A, 2, None, None, None) == E_DTYPE
+    # one-pass rollout: every argument error is found before the device query
+    op = L.trace_quant_rollout_onepass
+    assert op(A, 24, 1, 2, A, A, A, None, A, 0, None, None) == E_SIZE
+    assert op(A, n, 3, 2, A, A, A, None, A, 0, None, None) == E_SIZE
+    assert op(A, n, 1, 2, A, A, A, None, A, -1, None, None) == E_SIZE
+    assert op(A, n, 1, 2, A, A, A, None, None, 0, None, None) == E_NULL
+    assert op(A, n, 1, 2, None, A, A, None, A, 0, None, None) == E_NULL
+    assert op(A, n, 1, 2, A, A, A, None, A + 4, 0, None, None) == E_ALIGN
+    assert op(A, n, 1, 2, A, A, A, A + 8, A, 0, None, None) == E_ALIGN
+    assert op(A, n, 1, 2, A, A, A, None, A, 0, A + 2, None) == E_ALIGN
+    assert op(A, n, 1, 3, A, A, A, None, A, 0, None, None) == E_K
 
 
 def test_binding_rejects_cpu_tensors(tq):

@@ -81,8 +81,11 @@ class Checker:
     """Runs every entry point on the GPU once and compares chosen windows of
     blocks (or everything) with the oracle."""
 
-    def __init__(self, tq, X, Y, k, G=1):
+    def __init__(self, tq, X, Y, k, G=1, onepass=None):
+        """onepass: None = trace_amax + trace_quant_rollout; an int = the
+        one-pass rollout with that workgroup cap (0 = one per CU)."""
         self.tq, self.X, self.Y, self.k, self.G = tq, X, Y, k, G
+        self.onepass = onepass
         self.n = X.numel()
         self.nblk = self.n // 16
         self.Xh, self.Yh = h16(X), h16(Y)
@@ -92,9 +95,13 @@ class Checker:
         od = tq.OUT_F32 if out_f32 else tq.OUT_BF16
         r = {}
         st = torch.zeros(4, dtype=torch.int32, device=DEV)
-        r["gY"] = tq.amax(Y, G, status=st)
+        if self.onepass is None:
+            r["gY"] = tq.amax(Y, G, status=st)
+            r["codes"], r["scales"], r["gd"] = tq.quant_rollout(Y, r["gY"], k, G)
+        else:
+            r["gY"], r["codes"], r["scales"], r["gd"] = tq.quant_rollout_onepass(
+                Y, k, G, max_workgroups=self.onepass, status=st)
         r["gX"] = tq.amax(X, G)
-        r["codes"], r["scales"], r["gd"] = tq.quant_rollout(Y, r["gY"], k, G)
         r["pack"] = tq.guidance_pack(r["codes"], r["scales"], self.n, k)
         if k in (1, 2):
             r["yg"], r["cg"] = tq.fakequant_guided(X, r["gY"], r["gd"], k, G, od, codes_out=True)
@@ -492,3 +499,145 @@ def test_kv_one_buffer_two_groups(tq, wl):
         c = Checker(tq, X, Y, k, 2)
         c.run_gpu(out_f32=False)
         c.check(wins)
+
+
+# ---------------------------------------------------------------------------
+# One-pass rollout (amax and quantisation from one read): the same oracle
+# comparisons.  A small workgroup cap makes small tensors use every storage
+# path of a workgroup (registers, LDS, read twice) and group changes inside
+# a workgroup's run of tiles.
+# ---------------------------------------------------------------------------
+ONEPASS_SMALL = [  # (workload, rows, tensor index, workgroup caps)
+    (1, None, 0, (0, 1, 2)), (2, 2, 0, (0, 3)), (3, 1024, 0, (0, 3)), (4, 2048, 1, (0, 5)), (5, 1024, 2, (0, 7)),
+]
+
+
+@pytest.mark.parametrize("wl,rows,ti,caps", ONEPASS_SMALL)
+def test_onepass_small_full_parity(tq, wl, rows, ti, caps):
+    name, shape = synth.tensor_specs(wl, rows)[ti]
+    X, Y = synth.make_pair(wl, ti, shape, DEV)
+    for cap in caps:
+        for k in (1, 2, 4):
+            for G in (1, 4):
+                c = Checker(tq, X, Y, k, G, onepass=cap)
+                c.run_gpu(out_f32=False)
+                c.check()
+
+
+ONEPASS_FULL = [(2, 0, 1), (2, 0, 64), (3, 0, 1), (4, 0, 1), (5, 0, 1), (5, 1, 1)]
+
+
+@pytest.mark.parametrize("wl,ti,G", ONEPASS_FULL)
+def test_onepass_full_size_sampled(tq, wl, ti, G):
+    name, shape = synth.tensor_specs(wl)[ti]
+    X, Y = synth.make_pair(wl, ti, shape, DEV)
+    nblk = X.numel() // 16
+    rng = np.random.default_rng(wl * 100 + ti + 7)
+    amax_blk = int(torch.argmax(Y.float().abs().reshape(-1)).item()) // 16
+    wins = [(0, 600), (nblk - 600, nblk), (amax_blk - 40, amax_blk + 40)]
+    for s in rng.integers(0, nblk - 300, 6):
+        wins.append((int(s), int(s) + 300))
+    wins = blocks_of(nblk, wins)
+    for k in synth.WORKLOADS[wl].ks:
+        c = Checker(tq, X, Y, k, G, onepass=0)
+        c.run_gpu(out_f32=False)
+        c.check(wins)
+    del X, Y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_onepass_bruteforce(tq, k):
+    Yh = anchored_blocks()
+    nblk = Yh.size // 16
+    Y = to_dev_bf16(Yh)
+    for G, cap in ((nblk, 0), (nblk // 8 if nblk % 8 == 0 else 1, 0), (1, 5)):
+        c = Checker(tq, Y, Y, k, G, onepass=cap)
+        c.run_gpu(out_f32=False)
+        c.check()
+
+
+@pytest.mark.parametrize("nblk,G,cap", [(1, 1, 0), (2, 2, 0), (37, 1, 0), (3 * 512 + 6, 3, 1),
+                                        (2048 * 512 + 1234, 1, 0), (2048 * 513, 513, 0), (2048 * 513, 513, 9)])
+def test_onepass_sizes_and_degenerate(tq, nblk, G, cap):
+    rng = np.random.default_rng(nblk + cap)
+    x = rng.standard_normal(16 * nblk) * np.exp(rng.uniform(-3, 3, 16 * nblk))
+    X, Y = _pair_from_np(x, 0.01, nblk)
+    for k in (1, 2, 4):
+        c = Checker(tq, X, Y, k, G, onepass=cap)
+        c.run_gpu(out_f32=False)
+        if nblk > 100000:
+            c.check(blocks_of(nblk, [(0, 700), (nblk - 700, nblk), (nblk // 2, nblk // 2 + 700)]))
+        else:
+            c.check()
+    for case in ("zeros", "negzeros", "tiny"):
+        z = {"zeros": np.zeros(16 * 64), "negzeros": -np.zeros(16 * 64),
+             "tiny": rng.standard_normal(16 * 64) * 1e-39}[case]
+        X, Y = _pair_from_np(z, 0.02, 3)
+        c = Checker(tq, X, Y, 2, 1, onepass=cap)
+        c.run_gpu(out_f32=False)
+        c.check()
+
+
+def test_onepass_nonfinite_flag_and_repeat(tq):
+    x = np.ones(16 * 4096, np.float32)
+    x[5] = np.inf
+    x[7000] = np.nan
+    x[300] = 12.0
+    X = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    work = torch.empty(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
+    g, codes, scales, gd = tq.quant_rollout_onepass(X, 2, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -7
+    og, _ = oracle.amax(h16(X))
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+    # the same work buffer again, with a smaller input: cleared by the call
+    X2, Y2 = synth.make_pair(1, 0, (256, 2048), DEV)
+    st.zero_()
+    g2, c2, s2, gd2 = tq.quant_rollout_onepass(Y2, 2, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 0
+    og2, _ = oracle.amax(h16(Y2))
+    oc, os_, ogd = oracle.quant_rollout(h16(Y2), og2, 2)
+    assert_eq(g2.cpu().numpy().view(np.uint32), og2.view(np.uint32), "g")
+    assert_eq(h8(c2), oc, "codes")
+    assert_eq(h8(s2), os_, "scales")
+    assert_eq(h8(gd2), ogd, "guidance")
+
+
+def test_onepass_graph_replay_matches_eager(tq):
+    X, Y = synth.make_pair(2, 0, (4, 512, 2048), DEV)
+    n = Y.numel()
+    g = torch.empty(2, device=DEV)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=DEV)
+    gd = torch.empty(tq.guidance_bytes(n, 2), dtype=torch.uint8, device=DEV)
+    work = torch.empty(tq.onepass_work_bytes(2), dtype=torch.uint8, device=DEV)
+
+    def step():
+        tq.quant_rollout_onepass(Y, 2, 2, g=g, guidance=gd, codes=codes, scales=scales, work=work)
+
+    outs = (g, codes, scales, gd)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    og, _ = oracle.amax(h16(Y), 2)
+    assert_eq(ref[0].cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.view(torch.uint8).fill_(0xA5 if rep % 2 else 0x00)
+        work.fill_(0xFF if rep % 2 else 0x00)               # stale work contents must not matter
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
