@@ -5,12 +5,17 @@ tensor of the workload (default: routed-expert activations 64 experts x 512
 tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
 0.01, k = 2 guidance bits):
 
-  rollout   amax(Y) -> RTN quantise + guidance (k) -> full-code pack (k = 4)
+  rollout   amax(Y) + RTN quantise + guidance (k): the one-pass kernel (one
+            read of Y) when the tensor fits on chip, else amax(Y) then the
+            quantise kernel (--rollout picks either); full-code pack (k = 4)
   training  guided fake-quant (k) -> full-code fake-quant -> amax(X) ->
             plain RTN fake-quant with own scales
 
 `value` is the whole step's algorithmic bytes per second (GB/s) over K timed
-steps, replayed from a HIP graph; `roofline` is the guided fake-quant kernel
+steps, replayed from a HIP graph.  Algorithmic bytes: every operation of the
+step reads its inputs once and writes its outputs once (16.875 B per element
+at k = 2); a separate amax pass re-reads its input and is not counted there,
+only on its own per-kernel line.  `roofline` is the guided fake-quant kernel
 (the metric's subject) against the 8 TB/s HBM peak, its launch duration timed
 with HIP events on the stream it runs on over K back-to-back launches;
 `kernels` gives the same for every step kernel; `mismatch` holds the
@@ -34,8 +39,10 @@ DEFAULT_WORKLOAD = 2
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_expert_act_64x512x2048.txt")
 KERNEL_SRC = os.path.join(ROOT, "precision_numerics_block_amd", "csrc", "trace_quant.hip")
 
-KERNELS = ["amax_rollout", "quant_rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode",
-           "amax_training", "fakequant_rtn_own"]
+STEP = ["rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode", "amax_training",
+        "fakequant_rtn_own"]
+# per-kernel lines: the step's launches, and both rollout paths on their own
+KERNELS = STEP + ["rollout_onepass", "amax_rollout", "quant_rollout"]
 
 
 def parse():
@@ -50,6 +57,8 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
     p.add_argument("--separate-kv", action="store_true",
                    help="K and V as two tensors (G = 1 each) instead of one [2, T, H, D] buffer with G = 2")
+    p.add_argument("--rollout", choices=["auto", "onepass", "twopass"], default="auto",
+                   help="rollout path: auto = one-pass for tensors that fit on chip")
     p.add_argument("--cpu-elems", type=int, default=1 << 25, help="oracle sample size (elements)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain copy of this size (for counter calibration)")
@@ -57,17 +66,28 @@ def parse():
 
 
 def bytes_per_elem(k):
-    """Algorithmic bytes per element of each step kernel (read once, write once)."""
+    """Algorithmic bytes per element of each kernel line (read once, write once)."""
     gbits = k / 8.0
+    rollout = 2.0 + 0.5 + 1 / 16 + (1 / 16 + gbits)         # read y; codes, scales, guidance
     return {
+        "rollout": rollout,
+        "rollout_onepass": rollout,
         "amax_rollout": 2.0,
-        "quant_rollout": 2.0 + 0.5 + 1 / 16 + (1 / 16 + gbits),
+        "quant_rollout": rollout,
         "guidance_pack_full": (0.5 + 1 / 16) + (1 / 16 + 0.5),
         "fakequant_guided": 2.0 + (1 / 16 + gbits) + 2.0,
         "fakequant_fullcode": 2.0 + (1 / 16 + 0.5) + 2.0,
         "amax_training": 2.0,
         "fakequant_rtn_own": 2.0 + 2.0,
     }
+
+
+def step_bytes_per_elem(k):
+    """Algorithmic bytes per element of the whole step: each operation reads
+    its inputs once and writes its outputs once (the amax passes, which
+    re-read an input, are not algorithmic)."""
+    b = bytes_per_elem(k)
+    return sum(b[nm] for nm in STEP if not nm.startswith("amax"))
 
 
 def load_traffic():
@@ -107,7 +127,7 @@ def cpu_baseline(X, Y, n_sample, k):
     gx, _ = oracle.amax(Xh)
     oracle.fakequant_rtn(Xh, gx, codes=False)
     dt = time.perf_counter() - t0
-    step_bytes = sum(bytes_per_elem(k).values()) * n
+    step_bytes = step_bytes_per_elem(k) * n
     return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} elements of the first tensor's X and Y, whole step, {dt:.1f} s "
                       f"single-threaded C"}
@@ -288,14 +308,32 @@ def main():
             y_g=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_f=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
+            work=torch.zeros(max(tq.onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev),
         )
 
     bufs = [[make_bufs(shape, n, G) for shape, n, G in zip(shapes, ns, Gs)] for _ in range(2)]
+    # rollout path per tensor: one-pass when the tensor (in whole tiles of
+    # 8192 elements per group) fits on chip
+    cap = tq.onepass_capacity()
+    fits = [G * -(-(n // G) // 8192) * 8192 <= cap for n, G in zip(ns, Gs)]
+    onepass = [args.rollout == "onepass" or (args.rollout == "auto" and f) for f in fits]
+
+    def rollout(Y, b, G, one):
+        if one:
+            tq.quant_rollout_onepass(Y, k, G, g=b["g"], guidance=b["gd"], codes=b["codes"], scales=b["scales"],
+                                     work=b["work"])
+        else:
+            tq.amax(Y, G, out=b["g"])
+            tq.quant_rollout(Y, b["g"], k, G, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
 
     def launch(nm, i):
         """Kernel `nm` once on every tensor of input set i % 2."""
-        for (X, Y), b, n, G in zip(sets[i % 2], bufs[i % 2], ns, Gs):
-            if nm == "amax_rollout":
+        for (X, Y), b, n, G, one in zip(sets[i % 2], bufs[i % 2], ns, Gs, onepass):
+            if nm == "rollout":
+                rollout(Y, b, G, one)
+            elif nm == "rollout_onepass":
+                rollout(Y, b, G, True)
+            elif nm == "amax_rollout":
                 tq.amax(Y, G, out=b["g"])
             elif nm == "quant_rollout":
                 tq.quant_rollout(Y, b["g"], k, G, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
@@ -313,7 +351,7 @@ def main():
     # One stream: running the independent plain-QAT chain (amax(X) -> RTN) on
     # a second stream was measured slower (two HBM-bound chains interfere).
     def step(i):
-        for nm in KERNELS:
+        for nm in STEP:
             launch(nm, i)
 
     for i in range(args.warmup):
@@ -376,7 +414,7 @@ def main():
         per[nm] = a.elapsed_time(b_) / K                   # ms per launch of every tensor
 
     bpe = bytes_per_elem(k)
-    step_bytes = sum(bpe.values()) * n_total
+    step_bytes = step_bytes_per_elem(k) * n_total
     value = step_bytes / (ms_step * 1e-3) / 1e9
     g_ms = per["fakequant_guided"]
     g_bytes = bpe["fakequant_guided"] * n_total
@@ -426,7 +464,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{W.name} bf16 ({dist}, rollout relative noise {W.rel_noise}), k={k} "
                                f"guidance, G={max(Gs)}, whole rollout+training step",
-                   "tensors": [f"{nm} {'x'.join(map(str, sh))} G={G}" for (nm, sh), G in zip(names_shapes, Gs)],
+                   "tensors": [f"{nm} {'x'.join(map(str, sh))} G={G} rollout={'one-pass' if one else 'two-pass'}"
+                               for (nm, sh), G, one in zip(names_shapes, Gs, onepass)],
+                   "onepass_capacity_elements": cap,
                    "elements": n_total, "k": k, "G": max(Gs), "step_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,

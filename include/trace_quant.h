@@ -108,9 +108,17 @@ int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_d
 int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, int k,
                         uint8_t *codes, uint8_t *scales, uint8_t *guidance, void *stream);
 
-/* Bytes of the work buffer of trace_quant_rollout_onepass: 4352 + 4 G,
+/* Bytes of the work buffer of trace_quant_rollout_onepass: 8704 + 4 G,
  * rounded up to a multiple of 256 (0 if G < 1). */
 size_t trace_onepass_work_bytes(int G);
+
+/* Elements the one-pass rollout keeps on chip on the current device with at
+ * most max_workgroups workgroups (0 = one per compute unit): tensors up to
+ * this size (with G > 1, each group counted in whole tiles of 8192 elements)
+ * are read once; beyond it the excess is read twice and the two-kernel path
+ * (trace_amax + trace_quant_rollout) is usually faster.  0 on error (no
+ * device, max_workgroups < 0). */
+int64_t trace_onepass_capacity(int max_workgroups);
 
 /* One-pass rollout: the results of trace_amax followed by trace_quant_rollout
  * (bit for bit), from one read of y where it fits on chip.  The global scale
@@ -122,14 +130,17 @@ size_t trace_onepass_work_bytes(int G);
  * chip; the part that does not fit is read a second time.
  * y_bf16: bf16[n]; g_out: f32[G], written; k, codes, scales, guidance: as
  * trace_quant_rollout.  work: device buffer of trace_onepass_work_bytes(G)
- * bytes, 16-byte aligned, owned by the caller; the call clears it itself (a
- * fill kernel, so the call can be captured in a graph); calls that share a
- * work buffer must be ordered on one stream.  max_workgroups: 0 = one per
+ * bytes, 16-byte aligned, owned by the caller, zero-filled before its first
+ * use; every call leaves it zeroed again (the last workgroup to finish
+ * clears it), so no fill is needed between calls and the call is one kernel
+ * launch (graph-capturable); calls that share a work buffer must be ordered
+ * on one stream; after a call that reports TRACE_E_BARRIER the buffer must
+ * be zero-filled again.  max_workgroups: 0 = one per
  * compute unit; a smaller cap leaves compute units to concurrent work but
  * keeps less on chip.  status_dev: nullable int*, as trace_amax's
  * (TRACE_E_NONFINITE), and TRACE_E_BARRIER if the workgroups were not all
  * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s); the
- * outputs are then undefined.  Enqueues two kernels (clear, one-pass). */
+ * outputs are then undefined.  Enqueues one kernel. */
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);

@@ -700,7 +700,8 @@ constexpr int kOpStream = 8;                       // tiles in flight per lane w
 constexpr uint32_t kOpLine = TRACE_OP_LINE_WORDS;
 constexpr uint32_t kOpSubgroups = 16;
 constexpr uint32_t kOpTopWord = kOpSubgroups * kOpLine;
-constexpr uint32_t kOpAccWord = (kOpSubgroups + 1) * kOpLine;
+constexpr uint32_t kOpDoneWord = (kOpSubgroups + 1) * kOpLine;      // the same tree again, for departures
+constexpr uint32_t kOpAccWord = 2 * (kOpSubgroups + 1) * kOpLine;
 constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
 
 struct OnePass {
@@ -879,6 +880,23 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(compact_k1(c0) | (compact_k1(c1) << 8)), o.bits, cb, 0, 0);
 }
 
+// Count this workgroup into a two-level tree of counters at `base` (16
+// subgroup words and a top word, one line each); true for the caller whose
+// count completed the top word.  Thread 0 only.
+__device__ __forceinline__ bool tree_count(uint32_t *base, uint32_t P, bool *top_done)
+{
+    const uint32_t sub = blockIdx.x % kOpSubgroups;
+    const uint32_t members = (P - sub + kOpSubgroups - 1) / kOpSubgroups;
+    const uint32_t nsub = min(P, kOpSubgroups);
+    bool last = false;
+    if (__hip_atomic_fetch_add(base + sub * kOpLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1)
+        last = __hip_atomic_fetch_add(base + kOpSubgroups * kOpLine, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == nsub - 1;
+    if (top_done)
+        *top_done = last;
+    return last;
+}
+
 // kSpan: output descriptors over the workgroup's whole run (see Outs).
 template <int K, bool kOneGroup, bool kSpan>
 __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
@@ -886,6 +904,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     extern __shared__ u32x4 lds_tiles[];           // a.lds_tiles * 2 * kOpThreads chunks
     __shared__ uint32_t wmax[kOpThreads / 64];
     __shared__ int passed;
+    __shared__ bool leaving_last;
     __shared__ float gslot[kOpGroupSlots];
 
     const uint32_t P = gridDim.x;
@@ -972,13 +991,9 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     // the last member of a subgroup (all members' maxima performed before
     // their counts) counts into the top word, which everyone watches.
     if (threadIdx.x == 0) {
-        const uint32_t sub = blockIdx.x % kOpSubgroups;
-        const uint32_t members = (P - sub + kOpSubgroups - 1) / kOpSubgroups;
         const uint32_t nsub = min(P, kOpSubgroups);
         uint32_t *top = a.work + kOpTopWord;
-        if (__hip_atomic_fetch_add(a.work + sub * kOpLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            members - 1)
-            __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tree_count(a.work, P, nullptr);
         uint64_t t0 = (uint64_t)wall_clock64();
         int ok = 1;
         while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nsub) {
@@ -1065,12 +1080,21 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
             quant_block<K>(outs_for(w[q], live), w[q], b, block_amax_bits(b), live ? gscale(w[q].grp) : 0.0f);
         }
     }
-}
 
-__global__ void k_onepass_clear(uint32_t *work, uint32_t words)
-{
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x)
-        work[i] = 0u;
+    // ---- departure: the last workgroup out leaves the work buffer zeroed ---
+    // Every workgroup read the group maxima (into gslot, before a barrier)
+    // and passed the arrival barrier before counting out, so nothing reads
+    // the words the last one clears; the next call on the stream starts after
+    // this kernel has finished.
+    if (threadIdx.x == 0)
+        tree_count(a.work + kOpDoneWord, P, &leaving_last);
+    __syncthreads();
+    if (leaving_last) {
+        for (uint32_t i = threadIdx.x; i < 2 * (kOpSubgroups + 1); i += kOpThreads)
+            a.work[i * kOpLine] = 0u;
+        for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
+            a.work[kOpAccWord + i] = 0u;
+    }
 }
 
 // Guidance stream from codes + scales.  Each lane packs four chunks (two
@@ -1405,6 +1429,17 @@ size_t trace_onepass_work_bytes(int G)
     return ((size_t)onepass_work_words(G) * 4 + 255) / 256 * 256;
 }
 
+int64_t trace_onepass_capacity(int max_workgroups)
+{
+    OnePassDevice d;
+    if (max_workgroups < 0 || onepass_device(d) != TRACE_OK)
+        return 0;
+    int64_t grid = (int64_t)d.cus * d.per_cu;
+    if (max_workgroups > 0 && max_workgroups < grid)
+        grid = max_workgroups;
+    return grid * (int64_t)(kOpRegTiles + d.lds_tiles) * kOpTile * 8;
+}
+
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream)
@@ -1450,11 +1485,8 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     if (grid > (int64_t)a.items)
         grid = a.items;
     hipStream_t st = (hipStream_t)stream;
-    uint32_t words = onepass_work_words(G);
     size_t lds = (size_t)a.lds_tiles * kOpTile * 16;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_onepass_clear, dim3((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024), dim3(256), 0,
-                       st, (uint32_t *)work, words);
 #define TRACE_OP(KK, ONE, SPAN) \
     hipLaunchKernelGGL((k_quant_onepass<KK, ONE, SPAN>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
     if (G == 1) {                                      // one group: only the tensor's last tile can be short

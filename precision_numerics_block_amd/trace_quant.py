@@ -29,6 +29,7 @@ _SIGS = {
     "trace_quant_rollout": (_int, [_vp, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp]),
     "trace_guidance_pack": (_int, [_vp, _vp, _i64, _int, _vp, _vp]),
     "trace_onepass_work_bytes": (_sz, [_int]),
+    "trace_onepass_capacity": (_i64, [_int]),
     "trace_quant_rollout_onepass": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
@@ -53,7 +54,7 @@ OUT_BF16, OUT_F32 = 0, 1
 
 __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
-    "onepass_work_bytes", "quant_rollout_onepass",
+    "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
     "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
     "record_read", "xxh64",
@@ -139,11 +140,17 @@ def onepass_work_bytes(G=1):
     return int(lib.trace_onepass_work_bytes(int(G)))
 
 
+def onepass_capacity(max_workgroups=0):
+    """Elements the one-pass rollout keeps on chip on the current device."""
+    return int(lib.trace_onepass_capacity(int(max_workgroups)))
+
+
 def quant_rollout_onepass(y, k, G=1, g=None, guidance=True, codes=None, scales=None, work=None,
                           max_workgroups=0, status=None):
     """amax and quant_rollout from one read of y (where it fits on chip).
-    Returns (g, codes, scales, guidance); ``work`` may be a preallocated
-    uint8 GPU tensor of onepass_work_bytes(G) bytes."""
+    Returns (g, codes, scales, guidance).  ``work``: a uint8 GPU tensor of
+    onepass_work_bytes(G) bytes, zero-filled before its first use (every call
+    leaves it zeroed); a fresh zeroed one is allocated when None."""
     _need(y, torch.bfloat16, "y")
     n, dev = y.numel(), y.device
     g = torch.empty(G, dtype=torch.float32, device=dev) if g is None else g
@@ -153,7 +160,8 @@ def quant_rollout_onepass(y, k, G=1, g=None, guidance=True, codes=None, scales=N
         guidance = _u8(guidance_bytes(n, k), dev)
     elif guidance is False:
         guidance = None
-    work = _u8(max(onepass_work_bytes(G), 256), dev) if work is None else work
+    if work is None:
+        work = torch.zeros(max(onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev)
     _check("trace_quant_rollout_onepass", lib.trace_quant_rollout_onepass(
         _ptr(y), n, int(G), int(k), _ptr(g), _ptr(codes), _ptr(scales), _ptr(guidance), _ptr(work),
         int(max_workgroups), _ptr(status), _stream(dev)))

@@ -51,9 +51,10 @@ def test_sizes(tq):
     assert tq.code_bytes(17) == 0 and tq.code_bytes(0) == 0
     assert tq.version() >= 100
     assert tq.lib.trace_status_str(-7).decode().startswith("an input")
-    assert tq.onepass_work_bytes(1) == 4608 and tq.onepass_work_bytes(64) == 4608
-    assert tq.onepass_work_bytes(65) == 4864 and tq.onepass_work_bytes(0) == 0
+    assert tq.onepass_work_bytes(1) == 8960 and tq.onepass_work_bytes(64) == 8960
+    assert tq.onepass_work_bytes(65) == 9216 and tq.onepass_work_bytes(0) == 0
     assert "barrier" in tq.lib.trace_status_str(-10).decode()
+    assert tq.onepass_capacity(-1) == 0                 # argument error, before any device query
 
 
 def test_argument_errors_before_any_hip_call(tq):

@@ -527,6 +527,14 @@ def test_onepass_small_full_parity(tq, wl, rows, ti, caps):
 ONEPASS_FULL = [(2, 0, 1), (2, 0, 64), (3, 0, 1), (4, 0, 1), (5, 0, 1), (5, 1, 1)]
 
 
+def test_onepass_capacity(tq):
+    """The 64x512x2048 activation tensor (and a layer's K and V together)
+    fits on chip on one MI355X; a workgroup cap shrinks the capacity."""
+    cap = tq.onepass_capacity()
+    assert cap >= 64 * 512 * 2048, cap
+    assert 0 < tq.onepass_capacity(16) < cap
+
+
 @pytest.mark.parametrize("wl,ti,G", ONEPASS_FULL)
 def test_onepass_full_size_sampled(tq, wl, ti, G):
     name, shape = synth.tensor_specs(wl)[ti]
@@ -586,24 +594,28 @@ def test_onepass_nonfinite_flag_and_repeat(tq):
     x[300] = 12.0
     X = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
     st = torch.zeros(4, dtype=torch.int32, device=DEV)
-    work = torch.empty(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
+    work = torch.zeros(tq.onepass_work_bytes(2), dtype=torch.uint8, device=DEV)
     g, codes, scales, gd = tq.quant_rollout_onepass(X, 2, status=st, work=work)
     torch.cuda.synchronize()
     assert int(st[0]) == -7
+    assert bool((work == 0).all()), "the call leaves its work buffer zeroed"
     og, _ = oracle.amax(h16(X))
     assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
-    # the same work buffer again, with a smaller input: cleared by the call
+    # the same work buffer again, several calls with other sizes, groups and
+    # workgroup caps: each call finds it zeroed by the previous one
     X2, Y2 = synth.make_pair(1, 0, (256, 2048), DEV)
-    st.zero_()
-    g2, c2, s2, gd2 = tq.quant_rollout_onepass(Y2, 2, status=st, work=work)
-    torch.cuda.synchronize()
-    assert int(st[0]) == 0
-    og2, _ = oracle.amax(h16(Y2))
-    oc, os_, ogd = oracle.quant_rollout(h16(Y2), og2, 2)
-    assert_eq(g2.cpu().numpy().view(np.uint32), og2.view(np.uint32), "g")
-    assert_eq(h8(c2), oc, "codes")
-    assert_eq(h8(s2), os_, "scales")
-    assert_eq(h8(gd2), ogd, "guidance")
+    for G, cap in ((1, 0), (2, 0), (1, 3), (2, 5), (1, 0)):
+        st.zero_()
+        g2, c2, s2, gd2 = tq.quant_rollout_onepass(Y2, 2, G, status=st, work=work, max_workgroups=cap)
+        torch.cuda.synchronize()
+        assert int(st[0]) == 0
+        assert bool((work == 0).all())
+        og2, _ = oracle.amax(h16(Y2), G)
+        oc, os_, ogd = oracle.quant_rollout(h16(Y2), og2, 2, G)
+        assert_eq(g2.cpu().numpy().view(np.uint32), og2.view(np.uint32), f"g G={G} cap={cap}")
+        assert_eq(h8(c2), oc, f"codes G={G} cap={cap}")
+        assert_eq(h8(s2), os_, f"scales G={G} cap={cap}")
+        assert_eq(h8(gd2), ogd, f"guidance G={G} cap={cap}")
 
 
 def test_onepass_graph_replay_matches_eager(tq):
@@ -613,7 +625,7 @@ def test_onepass_graph_replay_matches_eager(tq):
     codes = torch.empty(n // 2, dtype=torch.uint8, device=DEV)
     scales = torch.empty(n // 16, dtype=torch.uint8, device=DEV)
     gd = torch.empty(tq.guidance_bytes(n, 2), dtype=torch.uint8, device=DEV)
-    work = torch.empty(tq.onepass_work_bytes(2), dtype=torch.uint8, device=DEV)
+    work = torch.zeros(tq.onepass_work_bytes(2), dtype=torch.uint8, device=DEV)
 
     def step():
         tq.quant_rollout_onepass(Y, 2, 2, g=g, guidance=gd, codes=codes, scales=scales, work=work)
@@ -635,9 +647,9 @@ def test_onepass_graph_replay_matches_eager(tq):
     for rep in range(4):
         for t in outs:
             t.view(torch.uint8).fill_(0xA5 if rep % 2 else 0x00)
-        work.fill_(0xFF if rep % 2 else 0x00)               # stale work contents must not matter
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for t, r in zip(outs, ref):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
+        assert bool((work == 0).all()), f"replay {rep} left the work buffer dirty"
