@@ -35,7 +35,8 @@
  *     448, subnormals kept;
  *   - RTN ties go to the even magnitude index (the even E2M1 mantissa);
  *   - guidance bits = the low k bits of the rollout's magnitude index
- *     (k = 1 is the mantissa bit), or the whole nibble (k = 4);
+ *     (k = 1 is the mantissa bit; k = 3 is the whole magnitude index, no
+ *     sign), or the whole nibble (k = 4);
  *   - the reconstructed rollout code is the code nearest (in value) to the
  *     training value whose low k bits match; any tie falls back to RTN;
  *   - dequantised output y = sign * fp32(fp32(val * s) * g).
@@ -258,17 +259,29 @@ int64_t oracle_guidance_bytes(int64_t n, int k)
     return oracle_bitplane_offset(n) + n * k / 8;
 }
 
+/* Element i's k bits sit at bit positions i*k .. i*k + k - 1 of the bit
+ * plane, least significant first (bit position p = bit p % 8 of byte p / 8);
+ * for k = 3 a field can straddle two bytes, so bits are moved one at a time. */
 static void put_bits(uint8_t *plane, int64_t i, int k, int value)
 {
-    int64_t bit = i * k;
-    int mask = (1 << k) - 1;
-    plane[bit / 8] = (uint8_t)((plane[bit / 8] & ~(mask << (bit % 8))) | ((value & mask) << (bit % 8)));
+    for (int j = 0; j < k; ++j) {
+        int64_t p = i * k + j;
+        uint8_t m = (uint8_t)(1u << (p % 8));
+        if ((value >> j) & 1)
+            plane[p / 8] = (uint8_t)(plane[p / 8] | m);
+        else
+            plane[p / 8] = (uint8_t)(plane[p / 8] & ~m);
+    }
 }
 
 static int get_bits(const uint8_t *plane, int64_t i, int k)
 {
-    int64_t bit = i * k;
-    return (plane[bit / 8] >> (bit % 8)) & ((1 << k) - 1);
+    int value = 0;
+    for (int j = 0; j < k; ++j) {
+        int64_t p = i * k + j;
+        value |= ((plane[p / 8] >> (p % 8)) & 1) << j;
+    }
+    return value;
 }
 
 static void put_nibble(uint8_t *codes, int64_t i, int nib)
@@ -382,7 +395,7 @@ static double pick_nearer(double lo, double hi, double r, float v)
 }
 
 /* Guided choice for one normalised training value v with guidance bits gb
- * (k = 1 or 2): returns the chosen nibble (sign bit = sign bit of v).
+ * (k = 1, 2 or 3): returns the chosen nibble (sign bit = sign bit of v).
  * [en] TRACE Core Concept: choose between the two adjacent E2M1 points,
  * favouring the one nearer the rollout's actual code; the rollout code is
  * reconstructed as the code nearest v whose low k index bits equal gb, and

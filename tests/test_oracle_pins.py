@@ -79,7 +79,7 @@ def test_worked_example_scalar(orc):
     jt, jr = orc.rtn_index(vt), orc.rtn_index(vr)
     assert E2M1[jt] == W["training_rtn"] and E2M1[jr] == W["rollout_rtn"]
     assert (E2M1[jt] - E2M1[jr]) * c == W["amplified_diff"]
-    for k in (1, 2):
+    for k in (1, 2, 3):
         nib = orc.guided_nibble(vt, k, jr & ((1 << k) - 1))
         assert E2M1[nib & 7] == W["guided_training"]
     assert E2M1[orc.fullcode_nibble(vt, jr) & 7] == W["guided_training"]
@@ -101,7 +101,7 @@ def test_worked_example_tensor(orc):
     X, Y = bf16_bits(x), bf16_bits(y)
     g, st_ = orc.amax(Y)
     assert st_ == 0 and g[0] == 1.0
-    for k in (1, 2):
+    for k in (1, 2, 3):
         codes, scales, gd = orc.quant_rollout(Y, g, k)
         assert orc.e4m3_value(scales[1]) == W["combined_scale"]
         rn = orc.unpack_nibbles(codes)
@@ -230,7 +230,7 @@ def _probe_points(lo, hi, thr):
     return pts
 
 
-@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("k", [1, 2, 3])
 def test_guided_matches_hand_table(orc, k):
     table = read_table()[k]
     assert len(table) == 7
@@ -294,7 +294,7 @@ finite_f32 = st.floats(min_value=-8.0, max_value=8.0, width=32, allow_nan=False)
 
 
 @settings(max_examples=3000, deadline=None)
-@given(v=finite_f32, k=st.sampled_from([1, 2]), gb=st.integers(0, 3))
+@given(v=finite_f32, k=st.sampled_from([1, 2, 3]), gb=st.integers(0, 7))
 def test_invariants_scalar(orc, v, k, gb):
     gb &= (1 << k) - 1
     v = np.float32(v)
@@ -316,6 +316,7 @@ def test_invariants_scalar(orc, v, k, gb):
         for r in (jl, jl + 1):
             sign = 8 if np.signbit(v) else 0
             assert orc.fullcode_nibble(v, sign | r) & 7 == r
+            assert orc.guided_nibble(v, 3, r) & 7 == r
             assert orc.guided_nibble(v, 2, r & 3) & 7 == r
             exc = (r == 5 and 2 < a <= 2.25) or (r == 7 and 4 < a <= 4.5)
             if not exc:
@@ -416,7 +417,7 @@ def test_layouts(orc):
     g, _ = orc.amax(Y)
     off = orc.bitplane_offset(n)
     assert off == 256 and orc.guidance_bytes(n, 2) == 256 + n // 4
-    for k in (1, 2, 4):
+    for k in (1, 2, 3, 4):
         codes, scales, gd = orc.quant_rollout(Y, g, k)
         nib = orc.unpack_nibbles(codes)
         np.testing.assert_array_equal(codes, (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8))
@@ -428,6 +429,42 @@ def test_layouts(orc):
         np.testing.assert_array_equal(vals, want)
         np.testing.assert_array_equal(orc.guidance_pack(codes, scales, n, k), gd)
     del rng
+
+
+def test_k3_bitplane_literal(orc):
+    """The 3-bit plane against bytes worked by hand (tests/golden/bitplane_k3.txt;
+    fields straddle byte boundaries).  The values are E2M1 points times 448:
+    the block maximum 6 * 448 = 2688 gives g = 1 and block scale 448, so every
+    value normalises exactly onto its own point and RTN returns its index."""
+    kv = {}
+    for line in open(os.path.join(GOLD, "bitplane_k3.txt")):
+        line = line.split("#")[0].split()
+        if line:
+            kv[line[0]] = line[1:]
+    idx = [int(t) for t in kv["indices"]]
+    want = bytes(int(t, 16) for t in kv["bytes"])
+    block = idx + [7, 0, 0, 0, 0, 0, 0, 0]          # the second half carries the block maximum
+    Y = bf16_bits(np.array([E2M1[j] for j in block], np.float32) * np.float32(448.0))
+    g, _ = orc.amax(Y)
+    assert g[0] == 1.0
+    codes, scales, gd = orc.quant_rollout(Y, g, 3)
+    assert orc.e4m3_value(scales[0]) == 448.0
+    np.testing.assert_array_equal(orc.unpack_nibbles(codes) & 7, np.array(block))
+    off = orc.bitplane_offset(16)
+    assert bytes(gd[off:off + 3]) == want
+    assert orc.guidance_bytes(16, 3) == off + 6
+
+
+def test_k3_equals_fullcode_with_own_sign(orc):
+    """k = 3 carries the whole magnitude index, so the reconstructed code is
+    +-value(gb) with v's sign: the choice equals the full-code choice with the
+    rollout sign replaced by v's."""
+    rng = np.random.default_rng(9)
+    vs = list(rng.uniform(-7, 7, 3000).astype(np.float32)) + [np.float32(x) for x in E2M1] + [np.float32(-0.0)]
+    for v in vs:
+        for gb in range(8):
+            sign = 8 if np.signbit(v) else 0
+            assert orc.guided_nibble(v, 3, gb) == orc.fullcode_nibble(v, sign | gb), (v, gb)
 
 
 def test_one_step_mismatch_statistic(orc):
