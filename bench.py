@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
-    p.add_argument("--k", type=int, default=2, choices=[1, 2], help="guidance bits of the compact stream")
+    p.add_argument("--k", type=int, default=2, choices=[1, 2, 3], help="guidance bits of the compact stream")
+    p.add_argument("--no-variants", action="store_true", help="skip the other guidance widths' kernel lines")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-transport", action="store_true", help="skip the guidance-transport measurements")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
@@ -131,6 +132,54 @@ def cpu_baseline(X, Y, n_sample, k):
     return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} elements of the first tensor's X and Y, whole step, {dt:.1f} s "
                       f"single-threaded C"}
+
+
+def variant_stats(tq, sets, bufs, ns, Gs, K, k_main):
+    """The other guidance widths (k = 1, 2, 3 besides the step's): rollout
+    quantise + guidance emit and guided fake-quant, per-kernel burst timing
+    and the guided mismatch against the rollout codes."""
+    import torch
+
+    out = {}
+    n_total = sum(ns)
+    for k in (1, 2, 3):
+        if k == k_main:
+            continue
+        gds = [[torch.empty(tq.guidance_bytes(n, k), dtype=torch.uint8, device=b[0]["codes"].device)
+                for n in ns] for b in bufs]
+        lines = {}
+        for nm in ("quant_rollout", "fakequant_guided"):
+            def launch(i):
+                for (X, Y), b, gd, G in zip(sets[i % 2], bufs[i % 2], gds[i % 2], Gs):
+                    if nm == "quant_rollout":
+                        tq.quant_rollout(Y, b["g"], k, G, guidance=gd, codes=b["codes"], scales=b["scales"])
+                    else:
+                        tq.fakequant_guided(X, b["g"], gd, k, G, out=b["y_g"])
+            for i in range(2):
+                launch(i)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(K):
+                launch(i)
+            e.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(e) / K
+            bpe = (2.0 + 0.5 + 1 / 16 + 1 / 16 + k / 8) if nm == "quant_rollout" else (2.0 + 1 / 16 + k / 8 + 2.0)
+            gbs = bpe * n_total / (ms * 1e-3) / 1e9
+            lines[nm] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        # mismatch of the guided choice against the rollout's codes (set 0)
+        bad = tot = 0
+        for (X, Y), b, gd, G in zip(sets[0], bufs[0], gds[0], Gs):
+            tq.amax(Y, G, out=b["g"])
+            tq.quant_rollout(Y, b["g"], k, G, guidance=gd, codes=b["codes"], scales=b["scales"])
+            _, c = tq.fakequant_guided(X, b["g"], gd, k, G, codes_out=True)
+            d = c ^ b["codes"]                              # two nibbles (elements) per byte
+            bad += int(((d & 15) != 0).sum().item() + ((d >> 4) != 0).sum().item())
+            tot += 2 * b["codes"].numel()
+        lines["guidance_bits_per_element"] = round(8 * tq.guidance_bytes(ns[0], k) / ns[0], 4)
+        lines["mismatch_guided"] = round(bad / tot, 6)
+        out[f"k{k}"] = lines
+    return out
 
 
 def mismatch_stats(tq, pairs, bufs, k, Gs):
@@ -432,6 +481,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    variants = None if args.no_variants else variant_stats(tq, sets, bufs, ns, Gs, min(K, 20), k)
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
@@ -475,6 +525,7 @@ def main():
         "cpu_baseline": cpu,
         "mismatch": mism,
         "kernels": kernels,
+        "guidance_widths": variants,
         "transport": transport,
     }
     print(json.dumps(out))

@@ -32,11 +32,12 @@
  *
  * Guidance stream (a flat byte buffer, trace_guidance_bytes(n, k) long):
  *   [ scale plane: n/16 E4M3 bytes | zero pad up to a multiple of 256 | bits ]
- *   bits: element i's k bits at bit (i*k) mod 8 of byte floor(i*k/8) of the
- *   bit plane, least significant first.  k = 1: the mantissa bit of the
- *   rollout magnitude index; k = 2: its two low bits; k = 4: the whole nibble
- *   (the bit plane then equals the packed code array).  The global scales
- *   (f32[G]) travel beside the stream.
+ *   bits: element i's k bits at bit positions i*k .. i*k + k - 1 of the bit
+ *   plane (position p = bit p mod 8 of byte p / 8), least significant first.
+ *   k = 1: the mantissa bit of the rollout magnitude index; k = 2: its two
+ *   low bits; k = 3: the whole magnitude index without the sign (fields
+ *   straddle bytes); k = 4: the whole nibble (the bit plane then equals the
+ *   packed code array).  The global scales (f32[G]) travel beside the stream.
  *
  * Common rules for every entry point:
  *   - pointers are device pointers unless stated; the caller owns every
@@ -87,7 +88,7 @@ typedef enum { TRACE_OUT_BF16 = 0, TRACE_OUT_F32 = 1 } trace_out_dtype;
 size_t trace_code_bytes(int64_t n);
 /* Bytes of the block-scale array: n / 16. */
 size_t trace_scale_bytes(int64_t n);
-/* Bytes of the guidance stream for width k in {1, 2, 4}:
+/* Bytes of the guidance stream for width k in {1, 2, 3, 4}:
  * align256(n / 16) + n * k / 8. */
 size_t trace_guidance_bytes(int64_t n, int k);
 
@@ -102,7 +103,7 @@ int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_d
 
 /* Rollout quantisation with standard RTN ("TRACE Core Concept": the rollout
  * side's actual FP4 result), fused with the guidance emit.
- * y_bf16: bf16[n]; g: f32[G] from trace_amax; k in {1, 2, 4}.
+ * y_bf16: bf16[n]; g: f32[G] from trace_amax; k in {1, 2, 3, 4}.
  * codes: u8[n/2] packed nibbles; scales: u8[n/16] E4M3 block scales;
  * guidance: u8[trace_guidance_bytes(n, k)] or NULL (no guidance written). */
 int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, int k,
@@ -148,7 +149,7 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
 /* Guidance stream from existing codes and scales (for example an FP4 KV cache
  * written elsewhere); same layout as trace_quant_rollout's.  "TRACE Core
  * Concept", compact-guidance paragraph.  codes: u8[n/2]; scales: u8[n/16];
- * k in {1, 2, 4}; guidance: u8[trace_guidance_bytes(n, k)]. */
+ * k in {1, 2, 3, 4}; guidance: u8[trace_guidance_bytes(n, k)]. */
 int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, int k,
                         uint8_t *guidance, void *stream);
 
@@ -160,8 +161,9 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
  * low k index bits equal the guidance bits; the adjacent point nearer it is
  * chosen; ties fall back to RTN.
  * x_bf16: bf16[n]; g: f32[G] (the rollout's); guidance: a k-bit stream;
- * k in {1, 2}; y_out: bf16[n] or f32[n] per out_dtype; codes_out: nullable
- * u8[n/2] receiving the chosen nibbles. */
+ * k in {1, 2, 3} (k = 3, the whole magnitude index, decides like the full
+ * code with v's own sign); y_out: bf16[n] or f32[n] per out_dtype;
+ * codes_out: nullable u8[n/2] receiving the chosen nibbles. */
 int trace_fakequant_guided(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *guidance,
                            int k, void *y_out, int out_dtype, uint8_t *codes_out, void *stream);
 

@@ -371,6 +371,15 @@ __device__ __forceinline__ uint32_t compact_k2(uint32_t w)
     x = (x | (x >> 4)) & 0x00ff00ffu;
     return (x | (x >> 8)) & 0x0000ffffu;
 }
+// The 3-bit magnitude indices of 8 nibbles, packed LSB-first into 24 bits.
+__device__ __forceinline__ uint32_t compact_k3(uint32_t w)
+{
+    uint32_t x = w & 0x77777777u;
+    uint32_t y = (x & 0x07070707u) | ((x & 0x70707070u) >> 1);   // 6 bits per byte
+    uint32_t z = (y & 0x003f003fu) | ((y & 0x3f003f00u) >> 2);   // 12 bits per half
+    return (z & 0x00000fffu) | ((z & 0x0fff0000u) >> 4);
+}
+
 __device__ __forceinline__ uint32_t compact_k1(uint32_t w)
 {
     uint32_t x = w & 0x11111111u;
@@ -476,12 +485,29 @@ __device__ __forceinline__ void zero_pad(uint8_t *gd, uint32_t begin, uint32_t e
 template <int K>
 __device__ __forceinline__ void store_bits(uint8_t *gd_bits, uint32_t c, uint32_t cw)
 {
-    if (K == 4)
+    if (K == 4) {
         reinterpret_cast<uint32_t *>(gd_bits)[c] = cw;
-    else if (K == 2)
+    } else if (K == 3) {
+        // 3 bytes at 3c: a 2-byte store on the even-aligned side and a 1-byte
+        // store on the other (offsets chosen per lane, no divergent branch)
+        uint32_t b = compact_k3(cw), odd = c & 1u;
+        uint32_t o16 = 3 * c + odd, o8 = 3 * c + (odd ? 0u : 2u);
+        *reinterpret_cast<uint16_t *>(gd_bits + o16) = (uint16_t)(odd ? b >> 8 : b);
+        gd_bits[o8] = (uint8_t)(odd ? b : b >> 16);
+    } else if (K == 2) {
         reinterpret_cast<uint16_t *>(gd_bits)[c] = (uint16_t)compact_k2(cw);
-    else
+    } else {
         gd_bits[c] = (uint8_t)compact_k1(cw);
+    }
+}
+
+// The 24 guidance bits of chunk c of a k = 3 stream (the mirror of store_bits<3>).
+__device__ __forceinline__ uint32_t load_bits3(const uint8_t *gd_bits, uint32_t c)
+{
+    uint32_t odd = c & 1u;
+    uint32_t h = *reinterpret_cast<const uint16_t *>(gd_bits + 3 * c + odd);
+    uint32_t b = gd_bits[3 * c + (odd ? 0u : 2u)];
+    return odd ? (b | (h << 8)) : (h | (b << 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -872,9 +898,14 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.gds, cb / 2, 0, 0);
     const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.codes, cb * 4u, 0, TRACE_NT_STORE ? 2 : 0);
-    if (K == 4)
+    if (K == 4) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.bits, cb * 4u, 0, 0);
-    else if (K == 2)
+    } else if (K == 3) {                                        // 48 bits at 3 cb (even): three halves
+        uint32_t lo = compact_k3(c0), hi = compact_k3(c1);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)lo, o.bits, cb * 3u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((lo >> 16) | (hi << 8)), o.bits, cb * 3u + 2u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hi >> 8), o.bits, cb * 3u + 4u, 0, 0);
+    } else if (K == 2)
         __builtin_amdgcn_raw_buffer_store_b32(compact_k2(c0) | (compact_k2(c1) << 16), o.bits, cb * 2u, 0, 0);
     else
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(compact_k1(c0) | (compact_k1(c1) << 8)), o.bits, cb, 0, 0);
@@ -1114,6 +1145,12 @@ __global__ void __launch_bounds__(kThreads)
         reinterpret_cast<uint16_t *>(gd_scales)[q] = reinterpret_cast<const uint16_t *>(scales)[q];
         if (K == 4) {
             reinterpret_cast<u32x4 *>(gd_bits)[q] = cw;
+        } else if (K == 3) {                                 // 4 x 24 bits = 3 words at 12 q
+            uint32_t b0 = compact_k3(cw.x), b1 = compact_k3(cw.y), b2 = compact_k3(cw.z), b3 = compact_k3(cw.w);
+            uint32_t *p = reinterpret_cast<uint32_t *>(gd_bits) + 3 * q;
+            p[0] = b0 | (b1 << 24);
+            p[1] = (b1 >> 8) | (b2 << 16);
+            p[2] = (b2 >> 16) | (b3 << 8);
         } else if (K == 2) {
             u32x2 b = {compact_k2(cw.x) | (compact_k2(cw.y) << 16), compact_k2(cw.z) | (compact_k2(cw.w) << 16)};
             reinterpret_cast<u32x2 *>(gd_bits)[q] = b;
@@ -1128,13 +1165,15 @@ __global__ void __launch_bounds__(kThreads)
     }
 }
 
-// Training side, guided (MODE 1, 2: k guidance bits) or full code (MODE 4).
+// Training side, guided (MODE 1, 2, 3: k guidance bits) or full code (MODE 4).
 template <int MODE, bool kOneGroup, bool kCodes>
 __global__ void __launch_bounds__(kThreads)
     k_fakequant_guided(const u32x4 *x, uint32_t nchunk, const float *__restrict__ g, DivMagic dm,
                        uint32_t last_group, const uint8_t *__restrict__ scale_plane,
                        const uint8_t *__restrict__ bits, OutPtr out, uint32_t *__restrict__ codes_out)
 {
+    // MODE 3 (the whole magnitude index) decides like the full code with the
+    // sign taken from v, so it shares the full-code table
     constexpr int R = MODE == 1 ? 2 : MODE == 2 ? 4 : 8;
     __shared__ Entry tab[kSlots * R];
     load_table<R>(tab, MODE == 1 ? kTabK1.e : MODE == 2 ? kTabK2.e : kTabFull.e);
@@ -1155,6 +1194,8 @@ __global__ void __launch_bounds__(kThreads)
                     gb[u] = bits[c];
                 else if (MODE == 2)
                     gb[u] = reinterpret_cast<const uint16_t *>(bits)[c];
+                else if (MODE == 3)
+                    gb[u] = load_bits3(bits, c);
                 else
                     gb[u] = ld_stream(reinterpret_cast<const uint32_t *>(bits) + c);
             }
@@ -1191,6 +1232,8 @@ __global__ void __launch_bounds__(kThreads)
                     row = (gb[u] >> i) & 1u;
                 } else if (MODE == 2) {
                     row = (gb[u] >> (2 * i)) & 3u;
+                } else if (MODE == 3) {
+                    row = (gb[u] >> (3 * i)) & 7u;
                 } else {
                     uint32_t r = (gb[u] >> (4 * i)) & 0xfu;
                     row = r & 7u;
@@ -1452,7 +1495,7 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     if (!aligned16(y_bf16) || !aligned16(g_out) || !aligned16(codes) || !aligned16(scales) ||
         (guidance && !aligned16(guidance)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
         return TRACE_E_ALIGN;
-    if (k != 1 && k != 2 && k != 4)
+    if (k < 1 || k > 4)
         return TRACE_E_K;
     if (max_workgroups < 0)
         return TRACE_E_SIZE;
@@ -1492,14 +1535,17 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     if (G == 1) {                                      // one group: only the tensor's last tile can be short
         if (k == 1) TRACE_OP(1, true, true);
         else if (k == 2) TRACE_OP(2, true, true);
+        else if (k == 3) TRACE_OP(3, true, true);
         else TRACE_OP(4, true, true);
     } else if (a.cpg % kOpTile == 0) {                 // groups of whole tiles
         if (k == 1) TRACE_OP(1, false, true);
         else if (k == 2) TRACE_OP(2, false, true);
+        else if (k == 3) TRACE_OP(3, false, true);
         else TRACE_OP(4, false, true);
     } else {
         if (k == 1) TRACE_OP(1, false, false);
         else if (k == 2) TRACE_OP(2, false, false);
+        else if (k == 3) TRACE_OP(3, false, false);
         else TRACE_OP(4, false, false);
     }
 #undef TRACE_OP
@@ -1512,7 +1558,7 @@ size_t trace_scale_bytes(int64_t n) { return check_sizes(n, 1) ? 0 : (size_t)(n 
 
 size_t trace_guidance_bytes(int64_t n, int k)
 {
-    if (check_sizes(n, 1) || (k != 1 && k != 2 && k != 4))
+    if (check_sizes(n, 1) || (k < 1 || k > 4))
         return 0;
     return (size_t)(bitplane_offset(n) + n * k / 8);
 }
@@ -1550,7 +1596,7 @@ int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, in
     if (!aligned16(y_bf16) || !aligned16(g) || !aligned16(codes) || !aligned16(scales) ||
         (guidance && !aligned16(guidance)))
         return TRACE_E_ALIGN;
-    if (k != 1 && k != 2 && k != 4)
+    if (k < 1 || k > 4)
         return TRACE_E_K;
     Launch L = plan(n, G, stream);
     uint8_t *bits = guidance ? guidance + bitplane_offset(n) : nullptr;
@@ -1562,10 +1608,12 @@ int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, in
     if (L.one) {
         if (k == 1) TRACE_Q(1, true);
         else if (k == 2) TRACE_Q(2, true);
+        else if (k == 3) TRACE_Q(3, true);
         else TRACE_Q(4, true);
     } else {
         if (k == 1) TRACE_Q(1, false);
         else if (k == 2) TRACE_Q(2, false);
+        else if (k == 3) TRACE_Q(3, false);
         else TRACE_Q(4, false);
     }
 #undef TRACE_Q
@@ -1581,7 +1629,7 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
         return TRACE_E_NULL;
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(guidance))
         return TRACE_E_ALIGN;
-    if (k != 1 && k != 2 && k != 4)
+    if (k < 1 || k > 4)
         return TRACE_E_K;
     uint32_t nchunk = (uint32_t)(n / 8);
     uint32_t nquad = (nchunk + 3) / 4;
@@ -1596,6 +1644,9 @@ int trace_guidance_pack(const uint8_t *codes, const uint8_t *scales, int64_t n, 
                            pe);
     else if (k == 2)
         hipLaunchKernelGGL((k_guidance_pack<2>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
+                           pe);
+    else if (k == 3)
+        hipLaunchKernelGGL((k_guidance_pack<3>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
                            pe);
     else
         hipLaunchKernelGGL((k_guidance_pack<4>), grid, dim3(kThreads), 0, st, cp, scales, nchunk, guidance, bits, pb,
@@ -1613,13 +1664,15 @@ int trace_fakequant_guided(const void *x_bf16, int64_t n, int G, const float *g,
         return TRACE_E_NULL;
     if (!aligned16(guidance) || (codes_out && !aligned16(codes_out)))
         return TRACE_E_ALIGN;
-    if (k != 1 && k != 2)
+    if (k != 1 && k != 2 && k != 3)
         return TRACE_E_K;
     Launch L = plan(n, G, stream);
     OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
     const uint8_t *bits = guidance + bitplane_offset(n);
     if (k == 1)
         return launch_guided<1>(L, x_bf16, g, guidance, bits, out, codes_out);
+    if (k == 3)
+        return launch_guided<3>(L, x_bf16, g, guidance, bits, out, codes_out);
     return launch_guided<2>(L, x_bf16, g, guidance, bits, out, codes_out);
 }
 

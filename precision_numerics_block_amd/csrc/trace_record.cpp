@@ -156,7 +156,7 @@ int trace_record_to_host(const uint8_t *guidance, const float *g, int64_t n, int
     if (!guidance || !g || !record_host)
         return TRACE_E_NULL;
     if (!valid_args(n, k, G))
-        return k != 1 && k != 2 && k != 4 ? TRACE_E_K : TRACE_E_SIZE;
+        return k < 1 || k > 4 ? TRACE_E_K : TRACE_E_SIZE;
     Header h = make_header(n, k, G);
     if (record_bytes < kHeader + h.payload_bytes)
         return TRACE_E_SIZE;

@@ -47,7 +47,8 @@ def test_sizes(tq):
     assert tq.guidance_bytes(n, 4) == 256 + n // 2
     n = 16 * 256 * 3                         # scale plane exactly 768 bytes: no pad
     assert tq.guidance_bytes(n, 2) == 768 + n // 4
-    assert tq.guidance_bytes(n, 3) == 0
+    assert tq.guidance_bytes(n, 3) == 768 + 3 * n // 8
+    assert tq.guidance_bytes(n, 5) == 0 and tq.guidance_bytes(n, 0) == 0
     assert tq.code_bytes(17) == 0 and tq.code_bytes(0) == 0
     assert tq.version() >= 100
     assert tq.lib.trace_status_str(-7).decode().startswith("an input")
@@ -81,7 +82,7 @@ def test_argument_errors_before_any_hip_call(tq):
     assert L.trace_fakequant_guided(A, n, 1, A, A + 1, 2, A, 0, None, None) == E_ALIGN
     assert L.trace_fakequant_rtn(A, n, 1, A, A + 4, A, 0, None, None, None) == E_ALIGN
     # guidance width and output dtype
-    assert L.trace_quant_rollout(A, n, 1, A, 3, A, A, A, None) == E_K
+    assert L.trace_quant_rollout(A, n, 1, A, 5, A, A, A, None) == E_K
     assert L.trace_guidance_pack(A, A, n, 0, A, None) == E_K
     assert L.trace_fakequant_guided(A, n, 1, A, A, 4, A, 0, None, None) == E_K
     assert L.trace_fakequant_guided(A, n, 1, A, A, 2, A, 7, None, None) == E_DTYPE
@@ -96,7 +97,7 @@ def test_argument_errors_before_any_hip_call(tq):
     assert op(A, n, 1, 2, A, A, A, None, A + 4, 0, None, None) == E_ALIGN
     assert op(A, n, 1, 2, A, A, A, A + 8, A, 0, None, None) == E_ALIGN
     assert op(A, n, 1, 2, A, A, A, None, A, 0, A + 2, None) == E_ALIGN
-    assert op(A, n, 1, 3, A, A, A, None, A, 0, None, None) == E_K
+    assert op(A, n, 1, 5, A, A, A, None, A, 0, None, None) == E_K
 
 
 def test_binding_rejects_cpu_tensors(tq):

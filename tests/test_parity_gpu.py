@@ -103,7 +103,7 @@ class Checker:
                 Y, k, G, max_workgroups=self.onepass, status=st)
         r["gX"] = tq.amax(X, G)
         r["pack"] = tq.guidance_pack(r["codes"], r["scales"], self.n, k)
-        if k in (1, 2):
+        if k in (1, 2, 3):
             r["yg"], r["cg"] = tq.fakequant_guided(X, r["gY"], r["gd"], k, G, od, codes_out=True)
         else:
             r["yg"], r["cg"] = tq.fakequant_fullcode(X, r["gY"], r["gd"], G, od, codes_out=True)
@@ -147,7 +147,7 @@ class Checker:
         f32 = self.out_f32
         for b0, b1 in windows:
             e0, e1 = 16 * b0, 16 * b1
-            if k in (1, 2):
+            if k in (1, 2, 3):
                 yg, cg = oracle.fakequant_guided(self.Xh, gY, gd, k, G, f32, b0, b1)
             else:
                 yg, cg = oracle.fakequant_fullcode(self.Xh, gY, gd, G, f32, b0, b1)
@@ -178,7 +178,7 @@ SMALL = [  # (workload, rows, tensor index)
 def test_workload_small_full_parity(tq, wl, rows, ti):
     name, shape = synth.tensor_specs(wl, rows)[ti]
     X, Y = synth.make_pair(wl, ti, shape, DEV)
-    for k in synth.WORKLOADS[wl].ks + ((4,) if 4 not in synth.WORKLOADS[wl].ks else ()):
+    for k in sorted(set(synth.WORKLOADS[wl].ks) | {3, 4}):
         for G in (1, 4):
             c = Checker(tq, X, Y, k, G)
             c.run_gpu(out_f32=(k == 2 and G == 1))
@@ -237,7 +237,7 @@ def anchored_blocks():
     return np.concatenate(out).reshape(-1)
 
 
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_bruteforce_rollout_and_rtn(tq, k):
     Yh = anchored_blocks()
     nblk = Yh.size // 16
@@ -265,7 +265,7 @@ COMBOS = [(1.0, 0x38), (2.0 ** -10, 0x28), (1.0 / 2688.0, 0x7E), (3.7e-3, 0x5C),
           (1.0e20, 0x7E), (0.3, 0x00), (5.0e-3, 0x33)]
 
 
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_bruteforce_guided_all_bf16(tq, k, out_f32):
     vals = all_finite_bf16()                                       # 4080 blocks
@@ -315,7 +315,7 @@ def test_sizes_and_ragged_tails(tq, nblk, G):
     rng = np.random.default_rng(nblk)
     x = rng.standard_normal(16 * nblk) * np.exp(rng.uniform(-3, 3, 16 * nblk))
     X, Y = _pair_from_np(x, 0.01, nblk)
-    for k in (1, 2, 4):
+    for k in (1, 2, 3, 4):
         c = Checker(tq, X, Y, k, G)
         c.run_gpu(out_f32=(k == 1))
         if nblk > 100000:
@@ -344,7 +344,7 @@ def test_degenerate_inputs(tq, case):
         x[::16] = 6.0                                # block amax 6 -> t = 1 -> s = 1
         x[0] = 2688.0                                # tensor amax -> g = 1
     X, Y = _pair_from_np(x, 0.02, 11)
-    for k in (1, 2, 4):
+    for k in (1, 2, 3, 4):
         c = Checker(tq, X, Y, k, 1)
         c.run_gpu(out_f32=(k != 2))
         c.check()
@@ -373,7 +373,7 @@ def test_guard_bytes_untouched(tq):
     X, Y = synth.make_pair(1, 0, (n // 2048 + 1, 2048), DEV)
     X, Y = X.reshape(-1)[:n].contiguous(), Y.reshape(-1)[:n].contiguous()
     pad = 4096
-    for k in (1, 2, 4):
+    for k in (1, 2, 3, 4):
         gb = tq.guidance_bytes(n, k)
         big_codes = torch.full((n // 2 + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
         big_scales = torch.full((n // 16 + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
@@ -517,7 +517,7 @@ def test_onepass_small_full_parity(tq, wl, rows, ti, caps):
     name, shape = synth.tensor_specs(wl, rows)[ti]
     X, Y = synth.make_pair(wl, ti, shape, DEV)
     for cap in caps:
-        for k in (1, 2, 4):
+        for k in (1, 2, 3, 4):
             for G in (1, 4):
                 c = Checker(tq, X, Y, k, G, onepass=cap)
                 c.run_gpu(out_f32=False)
@@ -554,7 +554,7 @@ def test_onepass_full_size_sampled(tq, wl, ti, G):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_onepass_bruteforce(tq, k):
     Yh = anchored_blocks()
     nblk = Yh.size // 16
@@ -571,7 +571,7 @@ def test_onepass_sizes_and_degenerate(tq, nblk, G, cap):
     rng = np.random.default_rng(nblk + cap)
     x = rng.standard_normal(16 * nblk) * np.exp(rng.uniform(-3, 3, 16 * nblk))
     X, Y = _pair_from_np(x, 0.01, nblk)
-    for k in (1, 2, 4):
+    for k in (1, 2, 3, 4):
         c = Checker(tq, X, Y, k, G, onepass=cap)
         c.run_gpu(out_f32=False)
         if nblk > 100000:

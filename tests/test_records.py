@@ -54,7 +54,7 @@ def test_xxh64_matches_reference_package(tq):
         assert tq.xxh64(torch.from_numpy(b)) == xxhash.xxh64(b.tobytes()).intdigest(), L
 
 
-@pytest.mark.parametrize("k,G", [(1, 1), (2, 1), (4, 1), (2, 3)])
+@pytest.mark.parametrize("k,G", [(1, 1), (2, 1), (3, 1), (4, 1), (2, 3)])
 def test_record_layout_seal_and_check(tq, k, G):
     n = 16 * 300 * G
     g, gd = oracle_stream(n, k)
@@ -113,7 +113,7 @@ def test_record_rejects_damage(tq, tmp_path):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_record_round_trip_gpu(tq, k, tmp_path):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
