@@ -57,6 +57,14 @@ def lib():
             "oracle_fakequant_guided": (None, [vp, i64, i32, vp, vp, i32, i64, i64, vp, i32, vp]),
             "oracle_fakequant_fullcode": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp]),
             "oracle_fakequant_rtn": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp, vp]),
+            "oracle_mx_scale": (u8, [f32]),
+            "oracle_mx_scale_value": (f64, [u8]),
+            "oracle_mx_bitplane_offset": (i64, [i64]),
+            "oracle_mx_guidance_bytes": (i64, [i64, i32]),
+            "oracle_mx_quant_rollout": (None, [vp, i64, i32, i64, i64, vp, vp, vp]),
+            "oracle_mx_dequant": (f32, [i32, u8]),
+            "oracle_mx_fakequant_guided": (None, [vp, i64, vp, i32, i64, i64, vp, i32, vp]),
+            "oracle_mx_fakequant_rtn": (None, [vp, i64, vp, i64, i64, vp, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -212,3 +220,67 @@ def unpack_nibbles(codes):
     out[0::2] = codes & 0xF
     out[1::2] = codes >> 4
     return out
+
+
+# ---- MXFP4 variant (32-element blocks, E8M0 scales, no global scale) -----
+def mx_scale(amax):
+    return int(lib().oracle_mx_scale(float(amax)))
+
+
+def mx_scale_value(code):
+    return float(lib().oracle_mx_scale_value(int(code)))
+
+
+def mx_bitplane_offset(n):
+    return int(lib().oracle_mx_bitplane_offset(int(n)))
+
+
+def mx_guidance_bytes(n, k):
+    return int(lib().oracle_mx_guidance_bytes(int(n), int(k)))
+
+
+def mx_dequant(nibble, code):
+    return float(lib().oracle_mx_dequant(int(nibble), int(code)))
+
+
+def _mx_range(n, b0, b1):
+    return (0 if b0 is None else b0), (n // 32 if b1 is None else b1)
+
+
+def mx_quant_rollout(y, k, b0=None, b1=None, guidance=True, out=None):
+    """MX RTN quantisation: returns (codes u8[n/2], scales u8[n/32], guidance or None)."""
+    y = _u16(y).reshape(-1)
+    n = y.size
+    b0, b1 = _mx_range(n, b0, b1)
+    if out is None:
+        codes = np.zeros(n // 2, np.uint8)
+        scales = np.zeros(n // 32, np.uint8)
+        gd = np.zeros(mx_guidance_bytes(n, k), np.uint8) if guidance else None
+    else:
+        codes, scales, gd = out
+    lib().oracle_mx_quant_rollout(_p(y), n, k, b0, b1, _p(codes), _p(scales), _p(gd))
+    return codes, scales, gd
+
+
+def mx_fakequant_guided(x, guidance, k, out_f32=False, b0=None, b1=None, codes=True):
+    """Guided (k = 1, 2, 3) or full-code (k = 4) fake-quant with MX scales."""
+    x = _u16(x).reshape(-1)
+    n = x.size
+    gd = np.ascontiguousarray(guidance, np.uint8)
+    b0, b1 = _mx_range(n, b0, b1)
+    y, c = _outbufs(n, out_f32, codes)
+    lib().oracle_mx_fakequant_guided(_p(x), n, _p(gd), k, b0, b1, _p(y), int(out_f32), _p(c))
+    return y, c
+
+
+def mx_fakequant_rtn(x, scales_in=None, out_f32=False, b0=None, b1=None, codes=True):
+    """Plain RTN with MX scales: returns (y, codes or None, scales used)."""
+    x = _u16(x).reshape(-1)
+    n = x.size
+    sin = None if scales_in is None else np.ascontiguousarray(scales_in, np.uint8)
+    b0, b1 = _mx_range(n, b0, b1)
+    y, c = _outbufs(n, out_f32, codes)
+    so = np.zeros(n // 32, np.uint8)
+    lib().oracle_mx_fakequant_rtn(_p(x), n, _p(sin), b0, b1, _p(y), int(out_f32), _p(c), _p(so))
+    return y, c, (sin if sin is not None else so)
+

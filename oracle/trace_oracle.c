@@ -528,3 +528,138 @@ void oracle_fakequant_rtn(const uint16_t *x, int64_t n, int G, const float *g,
         }
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 variant: 32-element blocks, E8M0 shared scale, no global scale */
+/* ------------------------------------------------------------------ */
+
+/* OCP Microscaling Formats (MX) v1.0: a block of 32 FP4 (E2M1) elements
+ * shares one E8M0 scale X = 2^(code - 127).  The shared exponent is
+ * floor(log2(max |V|)) - emax, with emax = 2 the exponent of E2M1's largest
+ * normal (6 = 1.5 * 2^2); each element is V / X rounded to E2M1 (nearest,
+ * ties to even, saturating at 6).  Readings taken where the text leaves a
+ * choice: the exponent is clamped to E8M0's finite range [-127, 127]
+ * (codes 0 .. 254), and an all-zero block gets code 0.  The pages use the
+ * NVFP4-style two-level scale; this variant is the block format of gfx950's
+ * scaled FP4 conversions, kept beside it. */
+uint8_t oracle_mx_scale(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;
+    int e;
+    frexp((double)amax, &e);          /* amax = m * 2^e, m in [0.5, 1): floor(log2) = e - 1 */
+    int shared = (e - 1) - 2;
+    int code = shared + 127;
+    if (code < 0) code = 0;
+    if (code > 254) code = 254;
+    return (uint8_t)code;
+}
+
+double oracle_mx_scale_value(uint8_t code)
+{
+    return ldexp(1.0, (int)code - 127);
+}
+
+int64_t oracle_mx_bitplane_offset(int64_t n)
+{
+    int64_t sp = n / 32;
+    return (sp + 255) / 256 * 256;
+}
+
+int64_t oracle_mx_guidance_bytes(int64_t n, int k)
+{
+    return oracle_mx_bitplane_offset(n) + n * k / 8;
+}
+
+/* v = V / X, computed in double (exact: X is a power of two) and rounded
+ * once to float (exact too, except where V / X falls below the float normal
+ * range, far under the smallest nonzero E2M1 point). */
+static float mx_normalise(uint16_t h, uint8_t code)
+{
+    return (float)((double)oracle_bf16_to_f32(h) / oracle_mx_scale_value(code));
+}
+
+/* Rollout side, blocks of 32 [b0, b1): codes, E8M0 scale bytes, optional
+ * guidance (scale plane of n/32 bytes, zero pad to 256, then k bits). */
+void oracle_mx_quant_rollout(const uint16_t *y, int64_t n, int k, int64_t b0, int64_t b1,
+                             uint8_t *codes, uint8_t *scales, uint8_t *guidance)
+{
+    uint8_t *bits = guidance ? guidance + oracle_mx_bitplane_offset(n) : NULL;
+    for (int64_t b = b0; b < b1; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+            float a = fabsf(oracle_bf16_to_f32(y[32 * b + i]));
+            if (a > amax) amax = a;
+        }
+        uint8_t code = oracle_mx_scale(amax);
+        scales[b] = code;
+        if (guidance)
+            guidance[b] = code;
+        for (int i = 0; i < 32; ++i) {
+            int64_t e = 32 * b + i;
+            int nib = oracle_rtn_nibble(mx_normalise(y[e], code));
+            put_nibble(codes, e, nib);
+            if (bits)
+                put_bits(bits, e, k, k == 4 ? nib : (nib & 7));
+        }
+    }
+    if (guidance && b0 == 0)
+        for (int64_t p = n / 32; p < oracle_mx_bitplane_offset(n); ++p)
+            guidance[p] = 0;
+}
+
+/* Dequantised MX value: sign * val * X (exact). */
+float oracle_mx_dequant(int nib, uint8_t code)
+{
+    double y = e2m1_magnitude(nib & 7) * oracle_mx_scale_value(code);
+    return (nib & 8) ? -(float)y : (float)y;
+}
+
+/* Training side: guided (k = 1, 2, 3) or full code (k = 4) with the
+ * rollout's MX scales, over blocks of 32 [b0, b1). */
+void oracle_mx_fakequant_guided(const uint16_t *x, int64_t n, const uint8_t *guidance, int k, int64_t b0,
+                                int64_t b1, void *y_out, int out_f32, uint8_t *codes_out)
+{
+    const uint8_t *bits = guidance + oracle_mx_bitplane_offset(n);
+    for (int64_t b = b0; b < b1; ++b) {
+        uint8_t code = guidance[b];
+        for (int i = 0; i < 32; ++i) {
+            int64_t e = 32 * b + i;
+            float v = mx_normalise(x[e], code);
+            int gb = get_bits(bits, e, k);
+            int nib = (k == 4) ? oracle_fullcode_nibble(v, gb) : oracle_guided_nibble(v, k, gb);
+            store_out(y_out, out_f32, e, oracle_mx_dequant(nib, code));
+            if (codes_out)
+                put_nibble(codes_out, e, nib);
+        }
+    }
+}
+
+/* Plain RTN with MX scales: own scales from x (scales_in == NULL) or given. */
+void oracle_mx_fakequant_rtn(const uint16_t *x, int64_t n, const uint8_t *scales_in, int64_t b0, int64_t b1,
+                             void *y_out, int out_f32, uint8_t *codes_out, uint8_t *scales_out)
+{
+    for (int64_t b = b0; b < b1; ++b) {
+        uint8_t code;
+        if (scales_in) {
+            code = scales_in[b];
+        } else {
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(oracle_bf16_to_f32(x[32 * b + i]));
+                if (a > amax) amax = a;
+            }
+            code = oracle_mx_scale(amax);
+        }
+        if (scales_out)
+            scales_out[b] = code;
+        for (int i = 0; i < 32; ++i) {
+            int64_t e = 32 * b + i;
+            int nib = oracle_rtn_nibble(mx_normalise(x[e], code));
+            store_out(y_out, out_f32, e, oracle_mx_dequant(nib, code));
+            if (codes_out)
+                put_nibble(codes_out, e, nib);
+        }
+    }
+}
+

@@ -496,3 +496,88 @@ def test_one_step_mismatch_statistic(orc):
     gmis = (sv(gn) != sv(rn)) & ~(((rn & 7) == 0) & ((gn & 7) == 0))
     assert gmis.sum() < 0.2 * mis.sum()
     assert n == 256 * 2048
+
+
+# --------------------------------------------------------------------------
+# MXFP4 variant (32-element blocks, E8M0 scales)
+# --------------------------------------------------------------------------
+def read_mx():
+    scales, blocks = [], []
+    for line in open(os.path.join(GOLD, "mx_examples.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("scale"):
+            _, a, c = line.split()
+            scales.append((float(a), int(c)))
+        elif line.startswith("block"):
+            vals, codes = line[5:].split("->")
+            blocks.append(([float(t) for t in vals.split()], [int(t) for t in codes.split()]))
+    return scales, blocks
+
+
+def test_mx_hand_examples(orc):
+    scales, blocks = read_mx()
+    assert len(scales) >= 8 and len(blocks) >= 2
+    for amax, code in scales:
+        assert orc.mx_scale(amax) == code, (amax, code)
+    for vals, want in blocks:
+        y = np.zeros(32, np.float32)
+        y[: len(vals)] = vals
+        Y = bf16_bits(y)
+        assert np.array_equal(bits_to_f32(Y.astype(np.uint32) << 16)[: len(vals)], np.float32(vals))
+        codes, sc, gd = orc.mx_quant_rollout(Y, 2)
+        nib = orc.unpack_nibbles(codes)
+        np.testing.assert_array_equal(nib[: len(want)], want)
+        assert not nib[len(want):].any()
+        assert gd[0] == sc[0]
+
+
+def test_mx_range_and_exact_round_trip(orc):
+    """A nonzero block with an unclamped code has max |V / X| in [4, 8); E2M1
+    points times a power of two come back exactly, codes and values."""
+    rng = np.random.default_rng(12)
+    for e in (-120, -20, -3, 0, 5, 60, 120):
+        j = rng.integers(0, 8, 32)
+        j[0] = 7                                           # the block maximum is 6 * 2^e
+        sgn = rng.choice([0, 8], 32)
+        vals = np.array([E2M1[t] for t in j], np.float64) * np.where(sgn, -1.0, 1.0) * 2.0 ** e
+        Y = bf16_bits(vals.astype(np.float32))
+        codes, sc, gd = orc.mx_quant_rollout(Y, 4)
+        assert orc.mx_scale_value(sc[0]) == 2.0 ** e
+        nib = orc.unpack_nibbles(codes)
+        np.testing.assert_array_equal(nib & 7, j)
+        np.testing.assert_array_equal(((nib & 8) != 0) & (j != 0), (sgn == 8) & (j != 0))
+        for t in range(32):
+            assert orc.mx_dequant(nib[t], sc[0]) == np.float32(vals[t]) or (j[t] == 0)
+        yr, _, _ = orc.mx_fakequant_rtn(Y, out_f32=True)
+        np.testing.assert_array_equal(yr, vals.astype(np.float32))
+    for _ in range(200):
+        a = np.float32(np.exp(rng.uniform(-80, 80)))
+        c = orc.mx_scale(a)
+        if 0 < c < 254:
+            r = float(a) / orc.mx_scale_value(c)
+            assert 4.0 <= r < 8.0, (a, c, r)
+
+
+def test_mx_worked_example_and_rules(orc):
+    """The worked example in MX form: a block whose maximum is 6 has X = 1,
+    so 2.51 / 2.49 normalise to themselves; RTN gives 3 / 2, guided gives 2."""
+    x = np.zeros(32, np.float32)
+    y = np.zeros(32, np.float32)
+    x[0] = y[0] = 6.0
+    x[1], y[1] = 2.51, 2.49
+    X, Y = bf16_bits(x), bf16_bits(y)
+    for k in (1, 2, 3, 4):
+        codes, sc, gd = orc.mx_quant_rollout(Y, k)
+        assert orc.mx_scale_value(sc[0]) == 1.0
+        assert orc.unpack_nibbles(codes)[1] == 4                    # rollout: 2.49 -> 2
+        yr, _, _ = orc.mx_fakequant_rtn(X, scales_in=sc, out_f32=True)
+        assert yr[1] == 3.0                                         # training RTN: 2.51 -> 3
+        yg, cg = orc.mx_fakequant_guided(X, gd, k, out_f32=True)
+        assert yg[1] == 2.0                                         # guided: the rollout side's 2
+    # own scales agree with the rollout scales for the same tensor
+    _, _, so = orc.mx_fakequant_rtn(Y)
+    _, sc, _ = orc.mx_quant_rollout(Y, 2)
+    np.testing.assert_array_equal(so, sc)
+
