@@ -180,6 +180,41 @@ int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *
 int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales_in,
                         void *y_out, int out_dtype, uint8_t *codes_out, uint8_t *scales_out, void *stream);
 
+/* ---- MXFP4 variant -------------------------------------------------------
+ * The block format of gfx950's scaled FP4 conversions (OCP Microscaling
+ * Formats v1.0): blocks of 32 consecutive elements share one E8M0 scale X =
+ * 2^(code - 127); there is no global scale.  code = floor(log2(block amax))
+ * - 2 + 127 (2 = the exponent of E2M1's largest value, 6 = 1.5 * 2^2),
+ * clamped to 0 .. 254; an all-zero block gets code 0.  Elements are RTN(x / X)
+ * on the E2M1 grid (ties to even, saturating at 6); dequantised y = sign *
+ * val * X (exact).  The pages use the two-level NVFP4-style scale above; the
+ * guided rule of "TRACE Core Concept" is the same on MX-normalised values.
+ * Guidance stream: [ scale plane: n/32 E8M0 bytes | zero pad to a multiple of
+ * 256 | bits ], bits as above.  Sizes: n > 0, n % 32 == 0, n < 2^35; 16-byte
+ * aligned pointers; scale bytes 0 .. 254 (255, E8M0's NaN, is not accepted
+ * as input). */
+
+/* Bytes of the MX scale array: n / 32. */
+size_t trace_mx_scale_bytes(int64_t n);
+/* Bytes of the MX guidance stream, k in {1, 2, 3, 4}: align256(n/32) + n*k/8. */
+size_t trace_mx_guidance_bytes(int64_t n, int k);
+
+/* MX rollout quantisation: codes u8[n/2], E8M0 scales u8[n/32], guidance
+ * (nullable) u8[trace_mx_guidance_bytes(n, k)], k in {1, 2, 3, 4}. */
+int trace_mx_quant_rollout(const void *y_bf16, int64_t n, int k, uint8_t *codes, uint8_t *scales,
+                           uint8_t *guidance, void *stream);
+
+/* MX training side: guided (k = 1, 2, 3) or full code (k = 4) with the
+ * rollout's MX scales from the guidance stream; outputs as
+ * trace_fakequant_guided. */
+int trace_mx_fakequant_guided(const void *x_bf16, int64_t n, const uint8_t *guidance, int k, void *y_out,
+                              int out_dtype, uint8_t *codes_out, void *stream);
+
+/* MX plain RTN fake-quant: scales_in NULL = own scales from x (written to
+ * scales_out if given), else u8[n/32] scales. */
+int trace_mx_fakequant_rtn(const void *x_bf16, int64_t n, const uint8_t *scales_in, void *y_out, int out_dtype,
+                           uint8_t *codes_out, uint8_t *scales_out, void *stream);
+
 /* ---- guidance records (transport and persistence) ---------------------- */
 /*
  * "TRACE Core Concept": the rollout's guidance travels GPU -> CPU memory ->

@@ -158,12 +158,19 @@ uint16_t oracle_f32_to_bf16(float f)
     uint32_t u;
     memcpy(&u, &f, 4);
     uint32_t sign = u & 0x80000000u, mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u)                       /* NaN: a quiet NaN of the same sign */
+        return (uint16_t)((sign >> 16) | 0x7fc0u);
+    if (mag == 0x7f800000u)                      /* infinity converts to infinity */
+        return (uint16_t)((sign >> 16) | 0x7f80u);
     uint32_t lo = mag & 0xffff0000u, hi = lo + 0x10000u;
     float flo, fhi, fa;
     memcpy(&flo, &lo, 4);
     memcpy(&fhi, &hi, 4);
     memcpy(&fa, &mag, 4);
-    int w = nearer((double)flo, (double)fhi, (double)fa);
+    /* above the largest bf16 value the next candidate is 2^128 (IEEE 754
+     * rounding: overflow to infinity from the largest value plus half an ulp) */
+    double dhi = (hi == 0x7f800000u) ? ldexp(1.0, 128) : (double)fhi;
+    int w = nearer((double)flo, dhi, (double)fa);
     uint32_t pick;
     if (w < 0)
         pick = lo;

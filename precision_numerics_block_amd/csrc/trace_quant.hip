@@ -1318,6 +1318,181 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 variant: blocks of 32 elements with a power-of-two (E8M0) scale and no
+// global scale (OCP Microscaling Formats v1.0 conversion; the block format of
+// gfx950's scaled FP4 conversions).  Four consecutive lanes hold a block: the
+// block maximum is two DPP steps, the scale needs no division (code = bf16
+// exponent field - 2, i.e. floor(log2 amax) - 2 + 127, clamped at 0), and
+// normalising and dequantising are exact multiplies by powers of two.  RTN,
+// the guided tables and the stores are the ones above.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quad_max(uint32_t m)
+{
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xb1, 0xf, 0xf, false));   // lane ^ 1
+    return max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4e, 0xf, 0xf, false));  // lane ^ 2
+}
+
+// E8M0 code of a block from its amax (bf16 magnitude bits): the exponent
+// field e gives floor(log2 amax) = e - 127 for normal values; subnormal,
+// tiny and zero blocks clamp to code 0.
+__device__ __forceinline__ uint32_t mx_code(uint32_t a16)
+{
+    uint32_t e = a16 >> 7;
+    return e >= 2 ? e - 2 : 0u;
+}
+
+__device__ __forceinline__ float mx_scale(uint32_t code) { return __builtin_ldexpf(1.0f, (int)code - 127); }
+__device__ __forceinline__ float mx_inv(uint32_t code) { return __builtin_ldexpf(1.0f, 127 - (int)code); }
+
+template <int K>
+__global__ void __launch_bounds__(kThreads)
+    k_mx_quant_rollout(const u32x4 *__restrict__ y, uint32_t nchunk, uint32_t *__restrict__ codes,
+                       uint8_t *__restrict__ scales, uint8_t *__restrict__ gd_scales, uint8_t *__restrict__ gd_bits,
+                       uint32_t pad_begin, uint32_t pad_end)
+{
+    if (gd_scales)
+        zero_pad<kThreads>(gd_scales, pad_begin, pad_end);
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) {
+            cs[u] = t * kTile + u * kThreads + threadIdx.x;
+            xc[u] = cs[u] < nchunk ? load_chunk(y, cs[u]) : Chunk{{0u, 0u, 0u, 0u}};
+        }
+        if (cs[0] >= nchunk)
+            continue;
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t code = mx_code(quad_max(chunk_amax_bits(xc[u])));
+            uint32_t c = cs[u];
+            if (c >= nchunk)
+                continue;
+            if ((c & 3u) == 0) {
+                scales[c >> 2] = (uint8_t)code;
+                if (gd_scales)
+                    gd_scales[c >> 2] = (uint8_t)code;
+            }
+            uint32_t cw = rtn8(xc[u], mx_inv(code));
+            st_stream(cw, codes + c);
+            if (gd_scales)
+                store_bits<K>(gd_bits, c, cw);
+        }
+    }
+}
+
+// Training side with MX scales: guided (MODE 1, 2, 3) or full code (MODE 4).
+template <int MODE, bool kCodes>
+__global__ void __launch_bounds__(kThreads)
+    k_mx_fakequant_guided(const u32x4 *x, uint32_t nchunk, const uint8_t *__restrict__ scale_plane,
+                          const uint8_t *__restrict__ bits, OutPtr out, uint32_t *__restrict__ codes_out)
+{
+    constexpr int R = MODE == 1 ? 2 : MODE == 2 ? 4 : 8;
+    __shared__ Entry tab[kSlots * R];
+    load_table<R>(tab, MODE == 1 ? kTabK1.e : MODE == 2 ? kTabK2.e : kTabFull.e);
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll], sc[kUnroll], gb[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = t * kTile + u * kThreads + threadIdx.x;
+            cs[u] = c;
+            xc[u] = Chunk{{0u, 0u, 0u, 0u}};
+            sc[u] = 0u;
+            gb[u] = 0u;
+            if (c < nchunk) {
+                xc[u] = load_chunk(x, c);
+                sc[u] = scale_plane[c >> 2];
+                if (MODE == 1)
+                    gb[u] = bits[c];
+                else if (MODE == 2)
+                    gb[u] = reinterpret_cast<const uint16_t *>(bits)[c];
+                else if (MODE == 3)
+                    gb[u] = load_bits3(bits, c);
+                else
+                    gb[u] = ld_stream(reinterpret_cast<const uint32_t *>(bits) + c);
+            }
+        }
+        if (cs[0] >= nchunk)
+            continue;
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = cs[u];
+            if (c >= nchunk)
+                continue;
+            float s = mx_scale(sc[u]), inv = mx_inv(sc[u]);
+            float yv[8];
+            uint32_t nw = 0;
+            for (int i = 0; i < 8; ++i) {
+                uint32_t w = xc[u].w[i >> 1];
+                float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * inv;
+                uint32_t row, nib = 0;
+                bool allow = true;
+                if (MODE == 1) {
+                    row = (gb[u] >> i) & 1u;
+                } else if (MODE == 2) {
+                    row = (gb[u] >> (2 * i)) & 3u;
+                } else if (MODE == 3) {
+                    row = (gb[u] >> (3 * i)) & 7u;
+                } else {
+                    uint32_t r = (gb[u] >> (4 * i)) & 0xfu;
+                    row = r & 7u;
+                    allow = (r >> 3) == (as_u(v) >> 31);
+                }
+                yv[i] = decide<R, kCodes>(tab, v, row, allow, s, 1.0f, nib);
+                if (kCodes)
+                    nw |= nib << (4 * i);
+            }
+            store_y(out, c, yv);
+            if (kCodes)
+                st_stream(nw, codes_out + c);
+        }
+    }
+}
+
+// Plain RTN with MX scales: from scales_in (kOwn = false) or from x.
+template <bool kOwn, bool kCodes>
+__global__ void __launch_bounds__(kThreads)
+    k_mx_fakequant_rtn(const u32x4 *x, uint32_t nchunk, const uint8_t *__restrict__ scales_in, OutPtr out,
+                       uint32_t *__restrict__ codes_out, uint8_t *__restrict__ scales_out)
+{
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        Chunk xc[kUnroll];
+        uint32_t cs[kUnroll], sc[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = t * kTile + u * kThreads + threadIdx.x;
+            cs[u] = c;
+            xc[u] = Chunk{{0u, 0u, 0u, 0u}};
+            sc[u] = 0u;
+            if (c < nchunk) {
+                xc[u] = load_chunk(x, c);
+                if (!kOwn)
+                    sc[u] = scales_in[c >> 2];
+            }
+        }
+        if (cs[0] >= nchunk)
+            continue;
+        for (int u = 0; u < kUnroll; ++u) {
+            if (kOwn)
+                sc[u] = mx_code(quad_max(chunk_amax_bits(xc[u])));
+            uint32_t c = cs[u];
+            if (c >= nchunk)
+                continue;
+            if (kOwn && scales_out && (c & 3u) == 0)
+                scales_out[c >> 2] = (uint8_t)sc[u];
+            float s = mx_scale(sc[u]);
+            uint32_t cw = rtn8(xc[u], mx_inv(sc[u]));
+            float yv[8];
+            decode8(cw, yv);
+            for (int i = 0; i < 8; ++i)
+                yv[i] = yv[i] * s;                         // exact: a power of two
+            store_y(out, c, yv);
+            if (kCodes)
+                st_stream(cw, codes_out + c);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxN = int64_t(1) << 35;   // chunk indices (n / 8) fit in 32 bits
@@ -1713,6 +1888,123 @@ int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, co
     return launch_rtn<true>(L, x_bf16, g, nullptr, out, codes_out, scales_out);
 }
 
+// ---- MXFP4 variant --------------------------------------------------------
+static int mx_check_sizes(int64_t n)
+{
+    return (n <= 0 || n % 32 != 0 || n >= kMaxN) ? TRACE_E_SIZE : TRACE_OK;
+}
+
+static int64_t mx_bitplane_offset(int64_t n) { return (n / 32 + 255) / 256 * 256; }
+
+size_t trace_mx_scale_bytes(int64_t n) { return mx_check_sizes(n) ? 0 : (size_t)(n / 32); }
+
+size_t trace_mx_guidance_bytes(int64_t n, int k)
+{
+    if (mx_check_sizes(n) || k < 1 || k > 4)
+        return 0;
+    return (size_t)(mx_bitplane_offset(n) + n * k / 8);
+}
+
+int trace_mx_quant_rollout(const void *y_bf16, int64_t n, int k, uint8_t *codes, uint8_t *scales, uint8_t *guidance,
+                           void *stream)
+{
+    int rc = mx_check_sizes(n);
+    if (rc)
+        return rc;
+    if (!y_bf16 || !codes || !scales)
+        return TRACE_E_NULL;
+    if (!aligned16(y_bf16) || !aligned16(codes) || !aligned16(scales) || (guidance && !aligned16(guidance)))
+        return TRACE_E_ALIGN;
+    if (k < 1 || k > 4)
+        return TRACE_E_K;
+    uint32_t nchunk = (uint32_t)(n / 8);
+    uint8_t *bits = guidance ? guidance + mx_bitplane_offset(n) : nullptr;
+    uint32_t pb = (uint32_t)(n / 32), pe = (uint32_t)mx_bitplane_offset(n);
+    hipStream_t st = (hipStream_t)stream;
+    dim3 grid(grid_for(nchunk));
+    (void)hipGetLastError();
+#define TRACE_MQ(KK)                                                                                              \
+    hipLaunchKernelGGL((k_mx_quant_rollout<KK>), grid, dim3(kThreads), 0, st, (const u32x4 *)y_bf16, nchunk,     \
+                       (uint32_t *)codes, scales, guidance, bits, pb, pe)
+    if (k == 1) TRACE_MQ(1);
+    else if (k == 2) TRACE_MQ(2);
+    else if (k == 3) TRACE_MQ(3);
+    else TRACE_MQ(4);
+#undef TRACE_MQ
+    return launched();
+}
+
+int trace_mx_fakequant_guided(const void *x_bf16, int64_t n, const uint8_t *guidance, int k, void *y_out,
+                              int out_dtype, uint8_t *codes_out, void *stream)
+{
+    int rc = mx_check_sizes(n);
+    if (rc)
+        return rc;
+    if (!x_bf16 || !guidance || !y_out)
+        return TRACE_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(guidance) || !aligned16(y_out) || (codes_out && !aligned16(codes_out)))
+        return TRACE_E_ALIGN;
+    if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
+        return TRACE_E_DTYPE;
+    if (k < 1 || k > 4)
+        return TRACE_E_K;
+    uint32_t nchunk = (uint32_t)(n / 8);
+    const uint8_t *bits = guidance + mx_bitplane_offset(n);
+    OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
+    hipStream_t st = (hipStream_t)stream;
+    dim3 grid(grid_for(nchunk));
+    const u32x4 *xp = (const u32x4 *)x_bf16;
+    uint32_t *cp = (uint32_t *)codes_out;
+    (void)hipGetLastError();
+#define TRACE_MG(MODE)                                                                                             \
+    do {                                                                                                           \
+        if (cp)                                                                                                    \
+            hipLaunchKernelGGL((k_mx_fakequant_guided<MODE, true>), grid, dim3(kThreads), 0, st, xp, nchunk,      \
+                               guidance, bits, out, cp);                                                           \
+        else                                                                                                       \
+            hipLaunchKernelGGL((k_mx_fakequant_guided<MODE, false>), grid, dim3(kThreads), 0, st, xp, nchunk,     \
+                               guidance, bits, out, cp);                                                           \
+    } while (0)
+    if (k == 1) TRACE_MG(1);
+    else if (k == 2) TRACE_MG(2);
+    else if (k == 3) TRACE_MG(3);
+    else TRACE_MG(4);
+#undef TRACE_MG
+    return launched();
+}
+
+int trace_mx_fakequant_rtn(const void *x_bf16, int64_t n, const uint8_t *scales_in, void *y_out, int out_dtype,
+                           uint8_t *codes_out, uint8_t *scales_out, void *stream)
+{
+    int rc = mx_check_sizes(n);
+    if (rc)
+        return rc;
+    if (!x_bf16 || !y_out)
+        return TRACE_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(y_out) || (scales_in && !aligned16(scales_in)) ||
+        (codes_out && !aligned16(codes_out)) || (scales_out && !aligned16(scales_out)))
+        return TRACE_E_ALIGN;
+    if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
+        return TRACE_E_DTYPE;
+    uint32_t nchunk = (uint32_t)(n / 8);
+    OutPtr out{y_out, out_dtype == TRACE_OUT_F32};
+    hipStream_t st = (hipStream_t)stream;
+    dim3 grid(grid_for(nchunk));
+    const u32x4 *xp = (const u32x4 *)x_bf16;
+    uint32_t *cp = (uint32_t *)codes_out;
+    (void)hipGetLastError();
+#define TRACE_MR(OWN, CODES)                                                                                       \
+    hipLaunchKernelGGL((k_mx_fakequant_rtn<OWN, CODES>), grid, dim3(kThreads), 0, st, xp, nchunk, scales_in, out,  \
+                       cp, scales_out)
+    if (scales_in) {
+        if (cp) TRACE_MR(false, true); else TRACE_MR(false, false);
+    } else {
+        if (cp) TRACE_MR(true, true); else TRACE_MR(true, false);
+    }
+#undef TRACE_MR
+    return launched();
+}
+
 const char *trace_status_str(int status)
 {
     switch (status) {
@@ -1731,6 +2023,6 @@ const char *trace_status_str(int status)
     }
 }
 
-int trace_version(void) { return 400; }
+int trace_version(void) { return 500; }
 
 }  // extern "C"

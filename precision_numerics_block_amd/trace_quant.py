@@ -34,6 +34,11 @@ _SIGS = {
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_rtn": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp]),
+    "trace_mx_scale_bytes": (_sz, [_i64]),
+    "trace_mx_guidance_bytes": (_sz, [_i64, _int]),
+    "trace_mx_quant_rollout": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp]),
+    "trace_mx_fakequant_guided": (_int, [_vp, _i64, _vp, _int, _vp, _int, _vp, _vp]),
+    "trace_mx_fakequant_rtn": (_int, [_vp, _i64, _vp, _vp, _int, _vp, _vp, _vp]),
     "trace_record_bytes": (_sz, [_i64, _int, _int]),
     "trace_record_to_host": (_int, [_vp, _vp, _i64, _int, _int, _vp, _sz, _vp]),
     "trace_record_seal": (_int, [_vp, _sz]),
@@ -56,6 +61,7 @@ __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
     "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
+    "mx_scale_bytes", "mx_guidance_bytes", "mx_quant_rollout", "mx_fakequant_guided", "mx_fakequant_rtn",
     "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
     "record_read", "xxh64",
 ]
@@ -224,6 +230,55 @@ def fakequant_rtn(x, g, scales_in=None, G=1, out_dtype=OUT_BF16, out=None, codes
     _check("trace_fakequant_rtn", lib.trace_fakequant_rtn(
         _ptr(x), x.numel(), int(G), _ptr(g), _ptr(scales_in), _ptr(out), int(out_dtype),
         _ptr(codes_out), _ptr(scales_out), _stream(x.device)))
+    return out, codes_out, scales_out
+
+
+# ---- MXFP4 variant (32-element blocks, E8M0 scales, no global scale) ------
+def mx_scale_bytes(n):
+    return int(lib.trace_mx_scale_bytes(int(n)))
+
+
+def mx_guidance_bytes(n, k):
+    return int(lib.trace_mx_guidance_bytes(int(n), int(k)))
+
+
+def mx_quant_rollout(y, k, guidance=True, codes=None, scales=None):
+    """MX RTN codes u8[n/2], E8M0 scales u8[n/32] and (if ``guidance``) the
+    guidance stream of width k."""
+    _need(y, torch.bfloat16, "y")
+    n, dev = y.numel(), y.device
+    codes = _u8(n // 2, dev) if codes is None else codes
+    scales = _u8(n // 32, dev) if scales is None else scales
+    if guidance is True:
+        guidance = _u8(mx_guidance_bytes(n, k), dev)
+    elif guidance is False:
+        guidance = None
+    _check("trace_mx_quant_rollout", lib.trace_mx_quant_rollout(
+        _ptr(y), n, int(k), _ptr(codes), _ptr(scales), _ptr(guidance), _stream(dev)))
+    return codes, scales, guidance
+
+
+def mx_fakequant_guided(x, guidance, k, out_dtype=OUT_BF16, out=None, codes_out=None):
+    """MX guided (k = 1, 2, 3) or full-code (k = 4) fake-quant; returns (y, codes or None)."""
+    _need(x, torch.bfloat16, "x")
+    _need(guidance, torch.uint8, "guidance")
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    _check("trace_mx_fakequant_guided", lib.trace_mx_fakequant_guided(
+        _ptr(x), x.numel(), _ptr(guidance), int(k), _ptr(out), int(out_dtype), _ptr(codes_out), _stream(x.device)))
+    return out, codes_out
+
+
+def mx_fakequant_rtn(x, scales_in=None, out_dtype=OUT_BF16, out=None, codes_out=None, scales_out=None):
+    """MX plain RTN fake-quant; own scales when ``scales_in`` is None."""
+    _need(x, torch.bfloat16, "x")
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    if scales_out is True:
+        scales_out = _u8(x.numel() // 32, x.device)
+    elif scales_out is False:
+        scales_out = None
+    _check("trace_mx_fakequant_rtn", lib.trace_mx_fakequant_rtn(
+        _ptr(x), x.numel(), _ptr(scales_in), _ptr(out), int(out_dtype), _ptr(codes_out), _ptr(scales_out),
+        _stream(x.device)))
     return out, codes_out, scales_out
 
 

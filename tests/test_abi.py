@@ -55,6 +55,8 @@ def test_sizes(tq):
     assert tq.onepass_work_bytes(1) == 8960 and tq.onepass_work_bytes(64) == 8960
     assert tq.onepass_work_bytes(65) == 9216 and tq.onepass_work_bytes(0) == 0
     assert "barrier" in tq.lib.trace_status_str(-10).decode()
+    assert tq.mx_scale_bytes(32 * 10) == 10 and tq.mx_scale_bytes(16) == 0
+    assert tq.mx_guidance_bytes(32 * 10, 2) == 256 + 80 and tq.mx_guidance_bytes(32 * 10, 5) == 0
     assert tq.onepass_capacity(-1) == 0                 # argument error, before any device query
 
 
@@ -98,6 +100,16 @@ def test_argument_errors_before_any_hip_call(tq):
     assert op(A, n, 1, 2, A, A, A, A + 8, A, 0, None, None) == E_ALIGN
     assert op(A, n, 1, 2, A, A, A, None, A, 0, A + 2, None) == E_ALIGN
     assert op(A, n, 1, 5, A, A, A, None, A, 0, None, None) == E_K
+    # MX variant
+    assert L.trace_mx_quant_rollout(A, 48, 2, A, A, None, None) == E_SIZE
+    assert L.trace_mx_quant_rollout(A, n, 2, None, A, None, None) == E_NULL
+    assert L.trace_mx_quant_rollout(A, n, 2, A, A + 4, None, None) == E_ALIGN
+    assert L.trace_mx_quant_rollout(A, n, 0, A, A, None, None) == E_K
+    assert L.trace_mx_fakequant_guided(A, n, None, 2, A, 0, None, None) == E_NULL
+    assert L.trace_mx_fakequant_guided(A, n, A, 5, A, 0, None, None) == E_K
+    assert L.trace_mx_fakequant_guided(A, n, A, 2, A, 3, None, None) == E_DTYPE
+    assert L.trace_mx_fakequant_rtn(A, 16, None, A, 0, None, None, None) == E_SIZE
+    assert L.trace_mx_fakequant_rtn(A, n, A + 8, A, 0, None, None, None) == E_ALIGN
 
 
 def test_binding_rejects_cpu_tensors(tq):

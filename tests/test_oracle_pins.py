@@ -211,7 +211,11 @@ def test_bf16_rounding_matches_torch(orc):
     bits = rng.integers(0, 0x7F7F0000, 20000, dtype=np.uint32)
     ties = (bits & 0xFFFF0000) | 0x8000          # exact halfway cases
     near = (bits & 0xFFFF0000) | 0x7FFF
-    allb = np.concatenate([bits, ties, near, bits | 0x80000000, ties | 0x80000000])
+    top = np.arange(0x7F7F0000, 0x7F800001, 97, dtype=np.uint32)       # the top binade, overflow to inf
+    special = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F800000, 0x00000001, 0x00008000,
+                        0x00018000], np.uint32)
+    allb = np.concatenate([bits, ties, near, top, special, bits | 0x80000000, ties | 0x80000000,
+                           top | 0x80000000, special | 0x80000000])
     f = bits_to_f32(allb)
     ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = np.array([orc.f32_to_bf16(v) for v in f], np.uint16)
