@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     p.add_argument("--k", type=int, default=2, choices=[1, 2, 3], help="guidance bits of the compact stream")
-    p.add_argument("--no-variants", action="store_true", help="skip the other guidance widths' kernel lines")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the other guidance widths' and the MXFP4 variant's kernel lines")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-transport", action="store_true", help="skip the guidance-transport measurements")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
@@ -179,6 +180,61 @@ def variant_stats(tq, sets, bufs, ns, Gs, K, k_main):
         lines["guidance_bits_per_element"] = round(8 * tq.guidance_bytes(ns[0], k) / ns[0], 4)
         lines["mismatch_guided"] = round(bad / tot, 6)
         out[f"k{k}"] = lines
+    return out
+
+
+def mx_stats(tq, sets, ns, K, k):
+    """MXFP4 variant (32-element blocks, E8M0 scales): rollout quantise +
+    guidance, guided fake-quant and own-scale RTN, per-kernel burst timing
+    over the workload's tensors, and train/rollout code mismatch."""
+    import torch
+
+    dev = sets[0][0][0].device
+    n_total = sum(ns)
+    bufs = [[dict(codes=torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                  scales=torch.empty(n // 32, dtype=torch.uint8, device=dev),
+                  gd=torch.empty(tq.mx_guidance_bytes(n, k), dtype=torch.uint8, device=dev),
+                  y=torch.empty(n, dtype=torch.bfloat16, device=dev)) for n in ns] for _ in range(2)]
+    bpe = {"mx_quant_rollout": 2.0 + 0.5 + 1 / 32 + (1 / 32 + k / 8),
+           "mx_fakequant_guided": 2.0 + (1 / 32 + k / 8) + 2.0,
+           "mx_fakequant_rtn_own": 2.0 + 2.0}
+
+    def launch(nm, i):
+        for (X, Y), b in zip(sets[i % 2], bufs[i % 2]):
+            if nm == "mx_quant_rollout":
+                tq.mx_quant_rollout(Y.reshape(-1), k, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+            elif nm == "mx_fakequant_guided":
+                tq.mx_fakequant_guided(X.reshape(-1), b["gd"], k, out=b["y"])
+            else:
+                tq.mx_fakequant_rtn(X.reshape(-1), None, out=b["y"])
+
+    out = {}
+    for nm in bpe:
+        for i in range(2):
+            launch(nm, i)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(K):
+            launch(nm, i)
+        e.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(e) / K
+        gbs = bpe[nm] * n_total / (ms * 1e-3) / 1e9
+        out[nm] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    launch("mx_quant_rollout", 0)
+    bad_g = bad_r = tot = 0
+    for (X, Y), b in zip(sets[0], bufs[0]):
+        _, cg = tq.mx_fakequant_guided(X.reshape(-1), b["gd"], k, codes_out=True)
+        _, cr, _ = tq.mx_fakequant_rtn(X.reshape(-1), b["scales"], codes_out=True)
+        for c, acc in ((cg, "g"), (cr, "r")):
+            d = c ^ b["codes"]
+            m = int(((d & 15) != 0).sum().item() + ((d >> 4) != 0).sum().item())
+            if acc == "g":
+                bad_g += m
+            else:
+                bad_r += m
+        tot += 2 * b["codes"].numel()
+    out["mismatch"] = {"rtn_shared_scale": round(bad_r / tot, 6), f"guided_k{k}": round(bad_g / tot, 6)}
     return out
 
 
@@ -482,6 +538,7 @@ def main():
         torch.cuda.synchronize()
 
     variants = None if args.no_variants else variant_stats(tq, sets, bufs, ns, Gs, min(K, 20), k)
+    mx = None if args.no_variants else mx_stats(tq, sets, ns, min(K, 20), k)
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
@@ -526,6 +583,7 @@ def main():
         "mismatch": mism,
         "kernels": kernels,
         "guidance_widths": variants,
+        "mxfp4": mx,
         "transport": transport,
     }
     print(json.dumps(out))

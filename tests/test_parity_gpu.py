@@ -52,8 +52,12 @@ def to_dev_bf16(bits):
 def assert_f32_close(got, want, what):
     got = np.asarray(got, np.float32)
     want = np.asarray(want, np.float32)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: finite positions differ"
+    assert np.array_equal(got[~fin], want[~fin]), f"{what}: overflow values differ"
     err = np.abs(got.astype(np.float64) - want.astype(np.float64))
-    lim = REL_TOL * np.abs(want.astype(np.float64))
+    err[~fin] = 0.0
+    lim = REL_TOL * np.abs(np.where(fin, want, 0).astype(np.float64))
     bad = err > lim
     assert not bad.any(), f"{what}: {bad.sum()} outside rel {REL_TOL}, first at {np.argmax(bad)}"
     assert np.array_equal(np.signbit(got), np.signbit(want)), f"{what}: sign bits differ"

@@ -50,7 +50,10 @@ def eq(got, want, what):
 
 def close_f32(got, want, what):
     got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
-    bad = np.abs(got - want) > 1e-6 * np.abs(want)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: finite positions differ"
+    assert np.array_equal(got[~fin], want[~fin], equal_nan=True), f"{what}: overflow values differ"
+    bad = np.abs(got[fin] - want[fin]) > 1e-6 * np.abs(want[fin])
     assert not bad.any(), f"{what}: {bad.sum()} outside rel 1e-6"
     assert np.array_equal(np.signbit(got), np.signbit(want)), f"{what}: sign bits"
 
