@@ -414,6 +414,7 @@ def main():
             y_f=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             work=torch.zeros(max(tq.onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev),
+            st=torch.zeros(4, dtype=torch.int32, device=dev),
         )
 
     bufs = [[make_bufs(shape, n, G) for shape, n, G in zip(shapes, ns, Gs)] for _ in range(2)]
@@ -426,7 +427,7 @@ def main():
     def rollout(Y, b, G, one):
         if one:
             tq.quant_rollout_onepass(Y, k, G, g=b["g"], guidance=b["gd"], codes=b["codes"], scales=b["scales"],
-                                     work=b["work"])
+                                     work=b["work"], status=b["st"])
         else:
             tq.amax(Y, G, out=b["g"])
             tq.quant_rollout(Y, b["g"], k, G, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
@@ -537,6 +538,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    bad = [int(b["st"][0].item()) for bs in bufs for b in bs if int(b["st"][0].item()) != 0]
+    if bad:                                      # e.g. a one-pass launch whose workgroups were not all resident
+        raise RuntimeError(f"device status words report {bad} ({tq.lib.trace_status_str(bad[0]).decode()})")
     variants = None if args.no_variants else variant_stats(tq, sets, bufs, ns, Gs, min(K, 20), k)
     mx = None if args.no_variants else mx_stats(tq, sets, ns, min(K, 20), k)
     step(0)
