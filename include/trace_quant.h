@@ -140,8 +140,10 @@ int64_t trace_onepass_capacity(int max_workgroups);
  * compute unit; a smaller cap leaves compute units to concurrent work but
  * keeps less on chip.  status_dev: nullable int*, as trace_amax's
  * (TRACE_E_NONFINITE), and TRACE_E_BARRIER if the workgroups were not all
- * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s); the
- * outputs are then undefined.  Enqueues one kernel. */
+ * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s; the
+ * environment variable TRACE_ONEPASS_WAIT_US, read at each call, replaces it,
+ * which lets a test force the failure path); the outputs are then undefined.
+ * Enqueues one kernel. */
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);

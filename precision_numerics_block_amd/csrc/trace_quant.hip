@@ -35,6 +35,7 @@
 #include <bit>
 #include <cfloat>
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
 
 #include "trace_quant.h"
@@ -1688,8 +1689,11 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     a.pad_begin = (uint32_t)(n / 16);
     a.pad_end = (uint32_t)bitplane_offset(n);
     // the longest legitimate wait is one pass over y; allow 1 s plus y at 50 GB/s
+    // (TRACE_ONEPASS_WAIT_US replaces the limit: a test of the failure path)
     double secs = 1.0 + (double)n * 2.0 / 5.0e10;
-    a.wait_ticks = (uint64_t)(secs * (double)d.clock_khz * 1000.0);
+    if (const char *env = std::getenv("TRACE_ONEPASS_WAIT_US"))
+        secs = std::strtod(env, nullptr) * 1e-6;
+    a.wait_ticks = (uint64_t)(secs > 0.0 ? secs * (double)d.clock_khz * 1000.0 : 0.0);
     a.work = (uint32_t *)work;
     a.g_out = g_out;
     a.status = status_dev;

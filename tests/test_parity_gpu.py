@@ -657,3 +657,29 @@ def test_onepass_graph_replay_matches_eager(tq):
         for t, r in zip(outs, ref):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
         assert bool((work == 0).all()), f"replay {rep} left the work buffer dirty"
+
+
+def test_onepass_barrier_timeout_reported(tq, monkeypatch):
+    """The failure path of the bounded grid barrier, forced from the host with
+    a zero time limit: the workgroups that wait give up, every kernel exits,
+    and the status word reports TRACE_E_BARRIER.  The work buffer is then
+    zero-filled again, as the contract asks, and a normal call is exact."""
+    X, Y = synth.make_pair(2, 0, (8, 512, 2048), DEV)
+    work = torch.zeros(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    monkeypatch.setenv("TRACE_ONEPASS_WAIT_US", "0")
+    tq.quant_rollout_onepass(Y, 2, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -10
+    monkeypatch.delenv("TRACE_ONEPASS_WAIT_US")
+    work.zero_()
+    st.zero_()
+    g, codes, scales, gd = tq.quant_rollout_onepass(Y, 2, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 0 and bool((work == 0).all())
+    og, _ = oracle.amax(h16(Y))
+    oc, os_, ogd = oracle.quant_rollout(h16(Y), og, 2)
+    assert_eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    assert_eq(h8(codes), oc, "codes")
+    assert_eq(h8(gd), ogd, "guidance")
+
