@@ -788,7 +788,10 @@ __device__ __forceinline__ void load_item(const OnePass &a, const Item &w, bool 
 // Copy this lane's two chunks of an item straight into LDS slot j
 // (global_load_lds, 16 bytes: lane i of a wave lands at the wave's base +
 // 16 i, so chunk u * T + t sits at (2 j + u) * T + t).  Lanes past the
-// item's end load nothing; their slots are masked or never stored.
+// item's end load nothing; their slots are masked or never stored.  The
+// copies are non-temporal like every other streaming load: with the default
+// policy they measured 6 us slower (of 24 for phase 1) when the previous
+// kernel had just written its output.
 __device__ __forceinline__ void load_item_to_lds(const OnePass &a, const Item &w, u32x4 *lds, uint32_t j)
 {
     uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -797,7 +800,7 @@ __device__ __forceinline__ void load_item_to_lds(const OnePass &a, const Item &w
         u32x4 *dst = lds + ((2 * j + u) * kOpThreads + wave * 64);
         if (o < w.count)
             __builtin_amdgcn_global_load_lds(a.y + w.first + o, (__attribute__((address_space(3))) void *)dst, 16, 0,
-                                             0);
+                                             TRACE_NT_LOAD ? 2 : 0);
     }
 }
 
