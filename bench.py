@@ -8,8 +8,9 @@ tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
   rollout   amax(Y) + RTN quantise + guidance (k): the one-pass kernel (one
             read of Y) when the tensor fits on chip, else amax(Y) then the
             quantise kernel (--rollout picks either); full-code pack (k = 4)
-  training  guided fake-quant (k) -> full-code fake-quant -> amax(X) ->
-            plain RTN fake-quant with own scales
+  training  guided fake-quant (k) -> full-code fake-quant -> plain QAT:
+            amax(X) + RTN fake-quant with own scales (one-pass kernel when the
+            tensor fits on chip, else the two kernels)
 
 `value` is the whole step's algorithmic bytes per second (GB/s) over K timed
 steps, replayed from a HIP graph.  Algorithmic bytes: every operation of the
@@ -39,10 +40,10 @@ DEFAULT_WORKLOAD = 2
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_expert_act_64x512x2048.txt")
 KERNEL_SRC = os.path.join(ROOT, "precision_numerics_block_amd", "csrc", "trace_quant.hip")
 
-STEP = ["rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode", "amax_training",
-        "fakequant_rtn_own"]
-# per-kernel lines: the step's launches, and both rollout paths on their own
-KERNELS = STEP + ["rollout_onepass", "amax_rollout", "quant_rollout"]
+STEP = ["rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode", "qat_rtn_own"]
+# per-kernel lines: the step's launches, and both paths of each fused pair on their own
+KERNELS = STEP + ["rollout_onepass", "amax_rollout", "quant_rollout", "rtn_onepass", "amax_training",
+                  "fakequant_rtn_own"]
 
 
 def parse():
@@ -60,7 +61,7 @@ def parse():
     p.add_argument("--separate-kv", action="store_true",
                    help="K and V as two tensors (G = 1 each) instead of one [2, T, H, D] buffer with G = 2")
     p.add_argument("--rollout", choices=["auto", "onepass", "twopass"], default="auto",
-                   help="rollout path: auto = one-pass for tensors that fit on chip")
+                   help="rollout and plain-QAT paths: auto = one-pass for tensors that fit on chip")
     p.add_argument("--cpu-elems", type=int, default=1 << 25, help="oracle sample size (elements)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain copy of this size (for counter calibration)")
@@ -81,6 +82,8 @@ def bytes_per_elem(k):
         "fakequant_fullcode": 2.0 + (1 / 16 + 0.5) + 2.0,
         "amax_training": 2.0,
         "fakequant_rtn_own": 2.0 + 2.0,
+        "qat_rtn_own": 2.0 + 2.0,
+        "rtn_onepass": 2.0 + 2.0,
     }
 
 
@@ -414,6 +417,7 @@ def main():
             y_f=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             y_r=torch.empty(shape, dtype=torch.bfloat16, device=dev),
             work=torch.zeros(max(tq.onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev),
+            work2=torch.zeros(max(tq.onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev),
             st=torch.zeros(4, dtype=torch.int32, device=dev),
         )
 
@@ -423,6 +427,13 @@ def main():
     cap = tq.onepass_capacity()
     fits = [G * -(-(n // G) // 8192) * 8192 <= cap for n, G in zip(ns, Gs)]
     onepass = [args.rollout == "onepass" or (args.rollout == "auto" and f) for f in fits]
+
+    def qat_rtn(X, b, G, one):
+        if one:
+            tq.fakequant_rtn_onepass(X, G, g=b["gx"], out=b["y_r"], work=b["work2"], status=b["st"])
+        else:
+            tq.amax(X, G, out=b["gx"])
+            tq.fakequant_rtn(X, b["gx"], None, G, out=b["y_r"])
 
     def rollout(Y, b, G, one):
         if one:
@@ -439,6 +450,10 @@ def main():
                 rollout(Y, b, G, one)
             elif nm == "rollout_onepass":
                 rollout(Y, b, G, True)
+            elif nm == "qat_rtn_own":
+                qat_rtn(X, b, G, one)
+            elif nm == "rtn_onepass":
+                qat_rtn(X, b, G, True)
             elif nm == "amax_rollout":
                 tq.amax(Y, G, out=b["g"])
             elif nm == "quant_rollout":
@@ -575,7 +590,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{W.name} bf16 ({dist}, rollout relative noise {W.rel_noise}), k={k} "
                                f"guidance, G={max(Gs)}, whole rollout+training step",
-                   "tensors": [f"{nm} {'x'.join(map(str, sh))} G={G} rollout={'one-pass' if one else 'two-pass'}"
+                   "tensors": [f"{nm} {'x'.join(map(str, sh))} G={G} "
+                               f"rollout+qat={'one-pass' if one else 'two-kernel'}"
                                for (nm, sh), G, one in zip(names_shapes, Gs, onepass)],
                    "onepass_capacity_elements": cap,
                    "elements": n_total, "k": k, "G": max(Gs), "step_bytes": int(step_bytes)},

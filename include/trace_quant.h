@@ -148,6 +148,19 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);
 
+/* One-pass plain QAT fake-quant with own scales: the results of trace_amax
+ * on x followed by trace_fakequant_rtn with scales_in = NULL (bit for bit),
+ * from one read of x where it fits on chip (the same kernel design, work
+ * buffer, capacity, barrier limit and status words as
+ * trace_quant_rollout_onepass).  "Experimental Results": plain QAT is the
+ * unstable baseline; "Why Does FP4 Rollout 'Break' RL Training?": RTN with
+ * a global and a block scale.  g_out: f32[G], written; y_out: bf16[n] or
+ * f32[n] per out_dtype; codes_out (u8[n/2]) and scales_out (u8[n/16]) are
+ * nullable.  Enqueues one kernel. */
+int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
+                                uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups,
+                                int *status_dev, void *stream);
+
 /* Guidance stream from existing codes and scales (for example an FP4 KV cache
  * written elsewhere); same layout as trace_quant_rollout's.  "TRACE Core
  * Concept", compact-guidance paragraph.  codes: u8[n/2]; scales: u8[n/16];

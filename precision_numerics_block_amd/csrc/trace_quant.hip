@@ -60,8 +60,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef TRACE_NT_LOAD
 #define TRACE_NT_LOAD 1
 #endif
-#ifndef TRACE_NT_STORE
-#define TRACE_NT_STORE 0
+// Store policy per kernel family: 1 = non-temporal stores, 0 = default
+// policy.  TRACE_NT_STORE, when given, sets all three.  Timed inside the
+// rollout + guided + full-code + RTN sequence on gfx950: non-temporal stores
+// take the guided kernel from about 49 to 45 us at 64M bf16 elements and
+// leave the rollout quantiser unchanged, while they slow the own-scale RTN
+// kernel from about 40 to 43 us, so RTN keeps the default policy.
+#ifdef TRACE_NT_STORE
+#define TRACE_NT_STORE_QUANT TRACE_NT_STORE
+#define TRACE_NT_STORE_GUIDED TRACE_NT_STORE
+#define TRACE_NT_STORE_RTN TRACE_NT_STORE
+#endif
+#ifndef TRACE_NT_STORE_QUANT
+#define TRACE_NT_STORE_QUANT 1
+#endif
+#ifndef TRACE_NT_STORE_GUIDED
+#define TRACE_NT_STORE_GUIDED 1
+#endif
+#ifndef TRACE_NT_STORE_RTN
+#define TRACE_NT_STORE_RTN 0
 #endif
 #ifndef TRACE_PAIR_SPLIT
 #define TRACE_PAIR_SPLIT 1
@@ -276,14 +293,13 @@ __device__ __forceinline__ T ld_stream(const T *p)
 #endif
 }
 
-template <class T>
+template <bool kNt, class T>
 __device__ __forceinline__ void st_stream(T v, T *p)
 {
-#if TRACE_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    if constexpr (kNt)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
 }
 
 // 8 consecutive bf16 elements: element 2m is the low half of w[m].
@@ -451,15 +467,16 @@ struct OutPtr {
     int f32;
 };
 
+template <bool kNt>
 __device__ __forceinline__ void store_y(OutPtr o, uint32_t c, const float (&y)[8])
 {
     if (o.f32) {
         f32x4 *p = reinterpret_cast<f32x4 *>(o.y) + 2 * (size_t)c;
-        st_stream(f32x4{y[0], y[1], y[2], y[3]}, p);
-        st_stream(f32x4{y[4], y[5], y[6], y[7]}, p + 1);
+        st_stream<kNt>(f32x4{y[0], y[1], y[2], y[3]}, p);
+        st_stream<kNt>(f32x4{y[4], y[5], y[6], y[7]}, p + 1);
     } else {
         u32x4 w = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
-        st_stream(w, reinterpret_cast<u32x4 *>(o.y) + c);
+        st_stream<kNt>(w, reinterpret_cast<u32x4 *>(o.y) + c);
     }
 }
 
@@ -656,7 +673,7 @@ __device__ __forceinline__ void quant_lane(const Chunk (&xc)[U], const uint32_t 
         if (cs[u] >= lim)
             continue;
         uint32_t cw = rtn8(xc[u], inv[u]);
-        st_stream(cw, codes + cs[u]);
+        st_stream<TRACE_NT_STORE_QUANT>(cw, codes + cs[u]);
         if (gd_scales)
             store_bits<K>(gd_bits, cs[u], cw);
     }
@@ -707,6 +724,9 @@ __global__ void __launch_bounds__(kThreads)
 // block maximum needs no exchange between lanes and each output plane takes
 // one store per lane.
 // ---------------------------------------------------------------------------
+#ifndef TRACE_OP_NT_STORE
+#define TRACE_OP_NT_STORE 1
+#endif
 #ifndef TRACE_OP_REG_TILES
 #define TRACE_OP_REG_TILES 24
 #endif
@@ -732,7 +752,7 @@ constexpr uint32_t kOpAccWord = 2 * (kOpSubgroups + 1) * kOpLine;
 constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
 
 struct OnePass {
-    const u32x4 *y;
+    const u32x4 *y;         // the input (the rollout's y, or the training tensor x)
     uint32_t cpg;           // chunks per group
     uint32_t tpg;           // tiles per group
     uint32_t items;         // G * tpg
@@ -743,8 +763,9 @@ struct OnePass {
     uint32_t *work;
     float *g_out;
     int *status;
-    uint32_t *codes;
+    uint32_t *codes;        // rollout codes, or the fake-quant's chosen codes (nullable there)
     uint8_t *scales, *gd_scales, *gd_bits;
+    void *out;              // fake-quant output (bf16 or f32), else null
 };
 
 // Where the chunks of item it lie (all uniform): chunk u of thread t is
@@ -876,17 +897,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *p, uint3
 // the item's own slice, for groups whose last tile is short.  Items that are
 // not live get descriptors with no records.
 struct Outs {
-    __amdgpu_buffer_rsrc_t codes, scales, gds, bits;
+    __amdgpu_buffer_rsrc_t codes, scales, gds, bits, y;
     uint32_t c0;               // first chunk covered
 };
 
-template <int K>
+// OUT: 0 = rollout (codes, scales, guidance), 1 / 2 = fake-quant output in
+// bf16 / f32 (16 / 32 bytes per chunk) with optional codes and scales.
+template <int K, int OUT>
 __device__ __forceinline__ Outs outs_over(const OnePass &a, uint32_t c0, uint32_t n)
 {
-    const bool gd = a.gd_scales != nullptr;
-    return Outs{span_rsrc(a.codes + c0, n * 4u), span_rsrc(a.scales + c0 / 2, n / 2),
-                span_rsrc(gd ? a.gd_scales + c0 / 2 : a.scales, gd ? n / 2 : 0u),
-                span_rsrc(gd ? a.gd_bits + (size_t)c0 * K : a.scales, gd ? n * K : 0u), c0};
+    Outs o;                                            // fields a mode does not use stay unset
+    o.c0 = c0;
+    if constexpr (OUT == 0) {                          // codes and scales are required here
+        const bool gd = a.gd_scales != nullptr;
+        o.codes = span_rsrc(a.codes + c0, n * 4u);
+        o.scales = span_rsrc(a.scales + c0 / 2, n / 2);
+        o.gds = span_rsrc(gd ? a.gd_scales + c0 / 2 : a.scales, gd ? n / 2 : 0u);
+        o.bits = span_rsrc(gd ? a.gd_bits + (size_t)c0 * K : a.scales, gd ? n * K : 0u);
+    } else {                                           // codes and scales are optional here
+        constexpr uint32_t cb = OUT == 2 ? 32u : 16u;
+        const void *any = a.out;                       // a valid base for a descriptor with no records
+        o.codes = span_rsrc(a.codes ? (const void *)(a.codes + c0) : any, a.codes ? n * 4u : 0u);
+        o.scales = span_rsrc(a.scales ? (const void *)(a.scales + c0 / 2) : any, a.scales ? n / 2 : 0u);
+        o.y = span_rsrc(static_cast<uint8_t *>(a.out) + (size_t)c0 * cb, n * cb);
+    }
+    return o;
 }
 
 // Codes, scale byte and guidance bits of this lane's block of one item (raw
@@ -901,7 +936,7 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.scales, cb / 2, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.gds, cb / 2, 0, 0);
     const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.codes, cb * 4u, 0, TRACE_NT_STORE ? 2 : 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.codes, cb * 4u, 0, TRACE_OP_NT_STORE ? 2 : 0);
     if (K == 4) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.bits, cb * 4u, 0, 0);
     } else if (K == 3) {                                        // 48 bits at 3 cb (even): three halves
@@ -913,6 +948,62 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
         __builtin_amdgcn_raw_buffer_store_b32(compact_k2(c0) | (compact_k2(c1) << 16), o.bits, cb * 2u, 0, 0);
     else
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(compact_k1(c0) | (compact_k1(c1) << 8)), o.bits, cb, 0, 0);
+}
+
+// Plain RTN fake-quant of this lane's block (own block scale from its raw
+// amax bits ab and the group's g): optional codes and scale byte as in
+// quant_block, and the dequantised values y = (val * s) * g.  Those are
+// handed back to the load layout (one DPP swap per word: the even lane keeps
+// its first chunk and takes the odd lane's first, the odd lane keeps its
+// second and takes the even lane's second), so each lane stores chunks t and
+// T + t of the item: 16 B (bf16) or 32 B (f32) per chunk, contiguous across
+// the wave.
+template <int OUT>
+__device__ __forceinline__ void rtn_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv)
+{
+    const uint32_t t = threadIdx.x, odd = t & 1u;
+    const uint32_t cb = w.first - o.c0 + 2 * block_of_lane();
+    const uint32_t sc = block_scale(as_f(ab << 16), gv);
+    const float s = e4m3_decode(sc);
+    const float inv = inv_combined(s, gv);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.scales, cb / 2, 0, 0);
+    const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, o.codes, cb * 4u, 0, 0);
+    float ylo[8], yhi[8];
+    decode8(c0, ylo);
+    decode8(c1, yhi);
+    for (int i = 0; i < 8; ++i) {
+        ylo[i] = (ylo[i] * s) * gv;                     // signed value: the sign rides along
+        yhi[i] = (yhi[i] * s) * gv;
+    }
+    const uint32_t base = w.first - o.c0 + t;           // chunk of slot u = 0, in o's span
+    if (OUT == 1) {
+        uint32_t lo[4], hi[4], out0[4], out1[4];
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = pack_bf16(ylo[2 * i], ylo[2 * i + 1]);
+            hi[i] = pack_bf16(yhi[2 * i], yhi[2 * i + 1]);
+            uint32_t recv = pair_swap(odd ? lo[i] : hi[i]);
+            out0[i] = odd ? recv : lo[i];
+            out1[i] = odd ? hi[i] : recv;
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{out0[0], out0[1], out0[2], out0[3]}, o.y, base * 16u, 0,
+                                               TRACE_OP_NT_STORE ? 2 : 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{out1[0], out1[1], out1[2], out1[3]}, o.y,
+                                               (base + kOpThreads) * 16u, 0, TRACE_OP_NT_STORE ? 2 : 0);
+    } else {
+        uint32_t out0[8], out1[8];
+        for (int i = 0; i < 8; ++i) {
+            uint32_t recv = pair_swap(odd ? as_u(ylo[i]) : as_u(yhi[i]));
+            out0[i] = odd ? recv : as_u(ylo[i]);
+            out1[i] = odd ? as_u(yhi[i]) : recv;
+        }
+        for (int h = 0; h < 2; ++h) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{out0[4 * h], out0[4 * h + 1], out0[4 * h + 2], out0[4 * h + 3]},
+                                                   o.y, base * 32u + 16u * h, 0, TRACE_OP_NT_STORE ? 2 : 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{out1[4 * h], out1[4 * h + 1], out1[4 * h + 2], out1[4 * h + 3]},
+                                                   o.y, (base + kOpThreads) * 32u + 16u * h, 0, TRACE_OP_NT_STORE ? 2 : 0);
+        }
+    }
 }
 
 // Count this workgroup into a two-level tree of counters at `base` (16
@@ -933,7 +1024,9 @@ __device__ __forceinline__ bool tree_count(uint32_t *base, uint32_t P, bool *top
 }
 
 // kSpan: output descriptors over the workgroup's whole run (see Outs).
-template <int K, bool kOneGroup, bool kSpan>
+// OUT: 0 = rollout (codes, scales, guidance of width K); 1 / 2 = plain RTN
+// fake-quant with own block scales, output bf16 / f32 (K unused).
+template <int K, bool kOneGroup, bool kSpan, int OUT = 0>
 __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
 {
     extern __shared__ u32x4 lds_tiles[];           // a.lds_tiles * 2 * kOpThreads chunks
@@ -1082,25 +1175,33 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     // the run of chunks this workgroup owns (items are consecutive, and with
     // kSpan only the run's last item can be short)
     const Item w_first = item_at<kOneGroup>(a, i0), w_last = item_at<kOneGroup>(a, i0 + cnt - 1);
-    const Outs span = outs_over<K>(a, w_first.first, w_last.first + w_last.count - w_first.first);
-    const Outs none = outs_over<K>(a, 0u, 0u);      // no records: every store dropped
+    const Outs span = outs_over<K, OUT>(a, w_first.first, w_last.first + w_last.count - w_first.first);
+    const Outs none = outs_over<K, OUT>(a, 0u, 0u);  // no records: every store dropped
     auto outs_for = [&](const Item &w, bool live) {
         // An item that is not live stores nothing wherever it lies (a batch of
         // read-twice items can run past its last one into the LDS items).
         if (!live)
             return none;
-        return kSpan ? span : outs_over<K>(a, w.first, w.count);
+        return kSpan ? span : outs_over<K, OUT>(a, w.first, w.count);
     };
+    auto block_out = [&](const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv) {
+        if constexpr (OUT == 0)
+            quant_block<K>(o, w, b, ab, gv);
+        else
+            rtn_block<OUT>(o, w, b, ab, gv);
+    };
+    // (with span descriptors a register tile that is not live lies past the
+    // run's end, outside the records, so it needs no descriptor of its own)
 #pragma unroll
     for (int h = 0; h < kOpRegTiles; ++h) {
         Item w = item_at<kOneGroup>(a, p2_reg + h);
         bool live = p2_reg + h < i0 + cnt;
-        quant_block<K>(outs_for(w, live), w, hr[h], hab[h], live ? gscale(w.grp) : 0.0f);
+        block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live ? gscale(w.grp) : 0.0f);
     }
     for (uint32_t j = 0; j < nlds; ++j) {
         Item w = item_at<kOneGroup>(a, p2_lds + j);
         Blk b = block_from_lds(lds_tiles, j);
-        quant_block<K>(outs_for(w, true), w, b, block_amax_bits(b), gscale(w.grp));
+        block_out(outs_for(w, true), w, b, block_amax_bits(b), gscale(w.grp));
     }
     for (uint32_t j = 0; j < nstr; j += kOpStream) {
         Chunk x[kOpStream][2];
@@ -1112,7 +1213,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
         for (int q = 0; q < kOpStream; ++q) {
             bool live = j + q < nstr;
             Blk b = to_block(x[q]);
-            quant_block<K>(outs_for(w[q], live), w[q], b, block_amax_bits(b), live ? gscale(w[q].grp) : 0.0f);
+            block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live ? gscale(w[q].grp) : 0.0f);
         }
     }
 
@@ -1247,9 +1348,9 @@ __global__ void __launch_bounds__(kThreads)
                 if (kCodes)
                     nw |= nib << (4 * i);
             }
-            store_y(out, c, yv);
+            store_y<TRACE_NT_STORE_GUIDED>(out, c, yv);
             if (kCodes)
-                st_stream(nw, codes_out + c);
+                st_stream<TRACE_NT_STORE_GUIDED>(nw, codes_out + c);
         }
     }
 }
@@ -1314,9 +1415,9 @@ __global__ void __launch_bounds__(kThreads)
             decode8(cw, yv);
             for (int i = 0; i < 8; ++i)
                 yv[i] = (yv[i] * s[u]) * gg[u];         // signed value: the sign rides along
-            store_y(out, c, yv);
+            store_y<TRACE_NT_STORE_RTN>(out, c, yv);
             if (kCodes)
-                st_stream(cw, codes_out + c);
+                st_stream<TRACE_NT_STORE_RTN>(cw, codes_out + c);
         }
     }
 }
@@ -1377,7 +1478,7 @@ __global__ void __launch_bounds__(kThreads)
                     gd_scales[c >> 2] = (uint8_t)code;
             }
             uint32_t cw = rtn8(xc[u], mx_inv(code));
-            st_stream(cw, codes + c);
+            st_stream<TRACE_NT_STORE_QUANT>(cw, codes + c);
             if (gd_scales)
                 store_bits<K>(gd_bits, c, cw);
         }
@@ -1445,9 +1546,9 @@ __global__ void __launch_bounds__(kThreads)
                 if (kCodes)
                     nw |= nib << (4 * i);
             }
-            store_y(out, c, yv);
+            store_y<TRACE_NT_STORE_GUIDED>(out, c, yv);
             if (kCodes)
-                st_stream(nw, codes_out + c);
+                st_stream<TRACE_NT_STORE_GUIDED>(nw, codes_out + c);
         }
     }
 }
@@ -1489,9 +1590,9 @@ __global__ void __launch_bounds__(kThreads)
             decode8(cw, yv);
             for (int i = 0; i < 8; ++i)
                 yv[i] = yv[i] * s;                         // exact: a power of two
-            store_y(out, c, yv);
+            store_y<TRACE_NT_STORE_RTN>(out, c, yv);
             if (kCodes)
-                st_stream(cw, codes_out + c);
+                st_stream<TRACE_NT_STORE_RTN>(cw, codes_out + c);
         }
     }
 }
@@ -1662,6 +1763,52 @@ int64_t trace_onepass_capacity(int max_workgroups)
     return grid * (int64_t)(kOpRegTiles + d.lds_tiles) * kOpTile * 8;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The launch parameters shared by both one-pass entry points (arguments
+// already checked): the item layout, the barrier limit and the grid.
+int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work, int max_workgroups,
+                 int *status_dev, OnePass &a, int64_t &grid, size_t &lds)
+{
+    OnePassDevice d;
+    int rc = onepass_device(d);
+    if (rc != TRACE_OK)
+        return rc;
+    a = OnePass{};
+    uint32_t nchunk = (uint32_t)(n / 8);
+    a.y = (const u32x4 *)in_bf16;
+    a.cpg = nchunk / (uint32_t)G;
+    a.tpg = (a.cpg + kOpTile - 1) / kOpTile;
+    a.items = a.tpg * (uint32_t)G;                       // <= nchunk / 2 + G < 2^32
+    a.G = (uint32_t)G;
+    a.lds_tiles = d.lds_tiles;
+    a.pad_begin = (uint32_t)(n / 16);
+    a.pad_end = (uint32_t)bitplane_offset(n);
+    // the longest legitimate wait is one pass over the input; allow 1 s plus
+    // the input at 50 GB/s (TRACE_ONEPASS_WAIT_US replaces the limit: a test
+    // of the failure path)
+    double secs = 1.0 + (double)n * 2.0 / 5.0e10;
+    if (const char *env = std::getenv("TRACE_ONEPASS_WAIT_US"))
+        secs = std::strtod(env, nullptr) * 1e-6;
+    a.wait_ticks = (uint64_t)(secs > 0.0 ? secs * (double)d.clock_khz * 1000.0 : 0.0);
+    a.work = (uint32_t *)work;
+    a.g_out = g_out;
+    a.status = status_dev;
+    grid = (int64_t)d.cus * d.per_cu;
+    if (max_workgroups > 0 && max_workgroups < grid)
+        grid = max_workgroups;
+    if (grid > (int64_t)a.items)
+        grid = a.items;
+    lds = (size_t)a.lds_tiles * kOpTile * 16;
+    return TRACE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream)
@@ -1678,39 +1825,16 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
         return TRACE_E_K;
     if (max_workgroups < 0)
         return TRACE_E_SIZE;
-    OnePassDevice d;
-    if ((rc = onepass_device(d)) != TRACE_OK)
-        return rc;
     OnePass a;
-    uint32_t nchunk = (uint32_t)(n / 8);
-    a.y = (const u32x4 *)y_bf16;
-    a.cpg = nchunk / (uint32_t)G;
-    a.tpg = (a.cpg + kOpTile - 1) / kOpTile;
-    a.items = a.tpg * (uint32_t)G;                       // <= nchunk / 2 + G < 2^32
-    a.G = (uint32_t)G;
-    a.lds_tiles = d.lds_tiles;
-    a.pad_begin = (uint32_t)(n / 16);
-    a.pad_end = (uint32_t)bitplane_offset(n);
-    // the longest legitimate wait is one pass over y; allow 1 s plus y at 50 GB/s
-    // (TRACE_ONEPASS_WAIT_US replaces the limit: a test of the failure path)
-    double secs = 1.0 + (double)n * 2.0 / 5.0e10;
-    if (const char *env = std::getenv("TRACE_ONEPASS_WAIT_US"))
-        secs = std::strtod(env, nullptr) * 1e-6;
-    a.wait_ticks = (uint64_t)(secs > 0.0 ? secs * (double)d.clock_khz * 1000.0 : 0.0);
-    a.work = (uint32_t *)work;
-    a.g_out = g_out;
-    a.status = status_dev;
+    int64_t grid;
+    size_t lds;
+    if ((rc = onepass_plan(y_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds)) != TRACE_OK)
+        return rc;
     a.codes = (uint32_t *)codes;
     a.scales = scales;
     a.gd_scales = guidance;
     a.gd_bits = guidance ? guidance + bitplane_offset(n) : nullptr;
-    int64_t grid = (int64_t)d.cus * d.per_cu;
-    if (max_workgroups > 0 && max_workgroups < grid)
-        grid = max_workgroups;
-    if (grid > (int64_t)a.items)
-        grid = a.items;
     hipStream_t st = (hipStream_t)stream;
-    size_t lds = (size_t)a.lds_tiles * kOpTile * 16;
     (void)hipGetLastError();
 #define TRACE_OP(KK, ONE, SPAN) \
     hipLaunchKernelGGL((k_quant_onepass<KK, ONE, SPAN>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
@@ -1731,6 +1855,50 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
         else TRACE_OP(4, false, false);
     }
 #undef TRACE_OP
+    return launched();
+}
+
+int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
+                                uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups,
+                                int *status_dev, void *stream)
+{
+    int rc = check_sizes(n, G);
+    if (rc)
+        return rc;
+    if (!x_bf16 || !g_out || !y_out || !work)
+        return TRACE_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(g_out) || !aligned16(y_out) || (codes_out && !aligned16(codes_out)) ||
+        (scales_out && !aligned16(scales_out)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
+        return TRACE_E_ALIGN;
+    if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
+        return TRACE_E_DTYPE;
+    if (max_workgroups < 0)
+        return TRACE_E_SIZE;
+    OnePass a;
+    int64_t grid;
+    size_t lds;
+    if ((rc = onepass_plan(x_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds)) != TRACE_OK)
+        return rc;
+    a.codes = (uint32_t *)codes_out;
+    a.scales = scales_out;
+    a.out = y_out;
+    hipStream_t st = (hipStream_t)stream;
+    bool f32 = out_dtype == TRACE_OUT_F32;
+    (void)hipGetLastError();
+#define TRACE_OR(ONE, SPAN)                                                                                        \
+    do {                                                                                                           \
+        if (f32)                                                                                                   \
+            hipLaunchKernelGGL((k_quant_onepass<2, ONE, SPAN, 2>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a); \
+        else                                                                                                       \
+            hipLaunchKernelGGL((k_quant_onepass<2, ONE, SPAN, 1>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a); \
+    } while (0)
+    if (G == 1)
+        TRACE_OR(true, true);
+    else if (a.cpg % kOpTile == 0)
+        TRACE_OR(false, true);
+    else
+        TRACE_OR(false, false);
+#undef TRACE_OR
     return launched();
 }
 

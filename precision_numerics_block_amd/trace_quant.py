@@ -31,6 +31,7 @@ _SIGS = {
     "trace_onepass_work_bytes": (_sz, [_int]),
     "trace_onepass_capacity": (_i64, [_int]),
     "trace_quant_rollout_onepass": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp]),
+    "trace_fakequant_rtn_onepass": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_rtn": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp]),
@@ -59,7 +60,7 @@ OUT_BF16, OUT_F32 = 0, 1
 
 __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
-    "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass",
+    "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass", "fakequant_rtn_onepass",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
     "mx_scale_bytes", "mx_guidance_bytes", "mx_quant_rollout", "mx_fakequant_guided", "mx_fakequant_rtn",
     "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
@@ -172,6 +173,27 @@ def quant_rollout_onepass(y, k, G=1, g=None, guidance=True, codes=None, scales=N
         _ptr(y), n, int(G), int(k), _ptr(g), _ptr(codes), _ptr(scales), _ptr(guidance), _ptr(work),
         int(max_workgroups), _ptr(status), _stream(dev)))
     return g, codes, scales, guidance
+
+
+def fakequant_rtn_onepass(x, G=1, g=None, out_dtype=OUT_BF16, out=None, codes_out=None, scales_out=None,
+                          work=None, max_workgroups=0, status=None):
+    """amax(x) and own-scale fakequant_rtn from one read of x (where it fits
+    on chip).  Returns (g, y, codes or None, scales or None); ``work`` as for
+    quant_rollout_onepass."""
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    g = torch.empty(G, dtype=torch.float32, device=dev) if g is None else g
+    out, codes_out = _outputs(x, out_dtype, out, codes_out)
+    if scales_out is True:
+        scales_out = _u8(x.numel() // 16, dev)
+    elif scales_out is False:
+        scales_out = None
+    if work is None:
+        work = torch.zeros(max(onepass_work_bytes(G), 256), dtype=torch.uint8, device=dev)
+    _check("trace_fakequant_rtn_onepass", lib.trace_fakequant_rtn_onepass(
+        _ptr(x), x.numel(), int(G), _ptr(g), _ptr(out), int(out_dtype), _ptr(codes_out), _ptr(scales_out),
+        _ptr(work), int(max_workgroups), _ptr(status), _stream(dev)))
+    return g, out, codes_out, scales_out
 
 
 def guidance_pack(codes, scales, n, k, out=None):

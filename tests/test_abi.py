@@ -100,6 +100,14 @@ def test_argument_errors_before_any_hip_call(tq):
     assert op(A, n, 1, 2, A, A, A, A + 8, A, 0, None, None) == E_ALIGN
     assert op(A, n, 1, 2, A, A, A, None, A, 0, A + 2, None) == E_ALIGN
     assert op(A, n, 1, 5, A, A, A, None, A, 0, None, None) == E_K
+    rop = L.trace_fakequant_rtn_onepass
+    assert rop(A, 24, 1, A, A, 0, None, None, A, 0, None, None) == E_SIZE
+    assert rop(A, n, 1, A, A, 0, None, None, None, 0, None, None) == E_NULL
+    assert rop(A, n, 1, None, A, 0, None, None, A, 0, None, None) == E_NULL
+    assert rop(A, n, 1, A, A + 2, 0, None, None, A, 0, None, None) == E_ALIGN
+    assert rop(A, n, 1, A, A, 0, A + 8, None, A, 0, None, None) == E_ALIGN
+    assert rop(A, n, 1, A, A, 5, None, None, A, 0, None, None) == E_DTYPE
+    assert rop(A, n, 1, A, A, 0, None, None, A, -2, None, None) == E_SIZE
     # MX variant
     assert L.trace_mx_quant_rollout(A, 48, 2, A, A, None, None) == E_SIZE
     assert L.trace_mx_quant_rollout(A, n, 2, None, A, None, None) == E_NULL

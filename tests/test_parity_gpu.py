@@ -683,3 +683,99 @@ def test_onepass_barrier_timeout_reported(tq, monkeypatch):
     assert_eq(h8(codes), oc, "codes")
     assert_eq(h8(gd), ogd, "guidance")
 
+
+# ---------------------------------------------------------------------------
+# One-pass plain QAT (amax(x) + own-scale RTN from one read): against the
+# oracle's amax and own-scale RTN
+# ---------------------------------------------------------------------------
+def check_rtn_onepass(tq, X, G, cap, out_f32, windows=None):
+    od = tq.OUT_F32 if out_f32 else tq.OUT_BF16
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    g, y, c, s = tq.fakequant_rtn_onepass(X, G, out_dtype=od, codes_out=True, scales_out=True,
+                                          max_workgroups=cap, status=st)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 0
+    Xh = h16(X)
+    og, _ = oracle.amax(Xh, G)
+    assert_eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    nblk = X.numel() // 16
+    for b0, b1 in (windows or [(0, nblk)]):
+        e0, e1 = 16 * b0, 16 * b1
+        oy, oc, os_ = oracle.fakequant_rtn(Xh, og, None, G, out_f32, b0, b1)
+        yy = y.reshape(-1)[e0:e1]
+        if out_f32:
+            assert_f32_close(yy.cpu().numpy(), oy[e0:e1], f"y {b0}:{b1}")
+        else:
+            assert_eq(h16(yy), oy[e0:e1], f"y {b0}:{b1}")
+        assert_eq(h8(c[e0 // 2:e1 // 2]), oc[e0 // 2:e1 // 2], f"codes {b0}:{b1}")
+        assert_eq(h8(s[b0:b1]), os_[b0:b1], f"scales {b0}:{b1}")
+
+
+@pytest.mark.parametrize("wl,rows,ti,caps", ONEPASS_SMALL)
+def test_rtn_onepass_small_full_parity(tq, wl, rows, ti, caps):
+    name, shape = synth.tensor_specs(wl, rows)[ti]
+    X, _ = synth.make_pair(wl, ti, shape, DEV)
+    for cap in caps:
+        for G in (1, 4):
+            for out_f32 in (False, True):
+                check_rtn_onepass(tq, X, G, cap, out_f32)
+
+
+@pytest.mark.parametrize("wl,ti,G", [(2, 0, 1), (2, 0, 64), (3, 0, 1), (5, 0, 1)])
+def test_rtn_onepass_full_size_sampled(tq, wl, ti, G):
+    name, shape = synth.tensor_specs(wl)[ti]
+    X, _ = synth.make_pair(wl, ti, shape, DEV)
+    nblk = X.numel() // 16
+    rng = np.random.default_rng(wl * 10 + ti + 3)
+    amax_blk = int(torch.argmax(X.float().abs().reshape(-1)).item()) // 16
+    wins = [(0, 600), (nblk - 600, nblk), (amax_blk - 40, amax_blk + 40)]
+    wins += [(int(s), int(s) + 300) for s in rng.integers(0, nblk - 300, 6)]
+    check_rtn_onepass(tq, X, G, 0, False, blocks_of(nblk, wins))
+    del X
+    torch.cuda.empty_cache()
+
+
+def test_rtn_onepass_bruteforce_and_sizes(tq):
+    Yh = anchored_blocks()
+    nblk = Yh.size // 16
+    X = to_dev_bf16(Yh)
+    for G, cap in ((nblk, 0), (1, 5)):
+        check_rtn_onepass(tq, X, G, cap, G == 1)
+    rng = np.random.default_rng(21)
+    for nb, G, cap in ((1, 1, 0), (37, 1, 0), (3 * 512 + 6, 3, 1), (2048 * 513, 513, 0)):
+        x = rng.standard_normal(16 * nb) * np.exp(rng.uniform(-3, 3, 16 * nb))
+        X, _ = _pair_from_np(x, 0.01, nb)
+        w = None if nb < 100000 else blocks_of(nb, [(0, 700), (nb - 700, nb), (nb // 2, nb // 2 + 700)])
+        check_rtn_onepass(tq, X, G, cap, False, w)
+
+
+def test_rtn_onepass_graph_replay_and_work_reuse(tq):
+    X, _ = synth.make_pair(2, 0, (4, 512, 2048), DEV)
+    g = torch.empty(1, device=DEV)
+    y = torch.empty_like(X)
+    work = torch.zeros(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
+    step = lambda: tq.fakequant_rtn_onepass(X, 1, g=g, out=y, work=work)  # noqa: E731
+    step()
+    torch.cuda.synchronize()
+    ref_g, ref_y = g.clone(), y.clone()
+    gx = tq.amax(X)
+    yr, _, _ = tq.fakequant_rtn(X, gx)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_g, gx) and torch.equal(ref_y.view(torch.int16), yr.view(torch.int16))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.view(torch.uint8).fill_(0xA5 if rep % 2 else 0)
+        g.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(g, ref_g), rep
+        assert bool((work == 0).all())
+
