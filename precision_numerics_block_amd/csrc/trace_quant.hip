@@ -263,6 +263,69 @@ __device__ __forceinline__ uint32_t block_scale(float ab, float g)
     return e4m3_encode(g > 0.0f ? q : 0.0f);
 }
 
+// Table-driven block scale of one group, equal to block_scale for every
+// finite block amax of the group.  A bf16 amax ab is V * 2^(e1 - 127) with
+// V = 1 + j/128 (exponent field e >= 1, e1 = e) or V = j/128 (e = 0, e1 = 1).
+// With d = fl(6g) = Dm * 2^Xd, Dm in [1, 2): ab / d = (V / Dm) * 2^E,
+// E = e1 - 127 - Xd, and because scaling by a power of two commutes with
+// rounding to fp32 in the normal range, fl(ab / d) = fl(V / Dm) * 2^E when
+// that is normal (when it is not, t < 2^-126 and the code is 0 either way).
+// So a 256-entry table indexed by (e > 0, j) holds q = fl(V / Dm) and the
+// E4M3 normal-range code of q, rebased so that adding 8 * e1 gives the code
+// of t (the RNE carry into the exponent is the same for q and t); 512 t is
+// ldexp(q, e1 + K).  A per-code table then gives 1 / (s * g).  Together they
+// replace two IEEE divisions and the E4M3 decode per block with two LDS reads
+// (the one-pass rollout's phase 2 is VALU-bound: 108 -> 72 VALU instructions
+// per register tile).
+__device__ __forceinline__ void split_pow2(float d, float &dm, int &xd)   // finite d > 0
+{
+    uint32_t u = as_u(d), e = u >> 23;
+    if (e == 0) {                                        // subnormal: normalise
+        int s = __clz(u) - 8;
+        u <<= s;
+        xd = -126 - s;
+    } else {
+        xd = (int)e - 127;
+    }
+    dm = as_f((u & 0x7fffffu) | 0x3f800000u);
+}
+
+__device__ __forceinline__ float2 scale_table_entry(uint32_t idx, float g)
+{
+    if (!(g > 0.0f))
+        return make_float2(0.0f, 0.0f);                  // t = 0 for every block: code 0
+    float dm;
+    int xd;
+    split_pow2(6.0f * g, dm, xd);
+    float v = idx >= 128u ? 1.0f + (float)(idx - 128u) * 0.0078125f : (float)idx * 0.0078125f;
+    float q = v / dm;
+    uint32_t u = as_u(q);
+    int32_t p = (int32_t)((u + 0x7ffffu + ((u >> 20) & 1u)) >> 20) - 960 - 8 * (127 + xd);
+    return make_float2(q, __int_as_float(p));
+}
+
+__device__ __forceinline__ int scale_table_k(float g)
+{
+    if (!(g > 0.0f))
+        return 0;
+    float dm;
+    int xd;
+    split_pow2(6.0f * g, dm, xd);
+    return -118 - xd;                                    // 9 - 127 - Xd
+}
+
+__device__ __forceinline__ uint32_t block_scale_tab(uint32_t hab, const float2 *tab, int k)
+{
+    uint32_t idx = min(hab, (hab & 127u) | 128u);        // (e > 0) * 128 + j
+    uint32_t e1 = max(hab >> 7, 1u);
+    float2 ent = tab[idx];
+    float tt = __builtin_amdgcn_ldexpf(ent.x, (int)e1 + k);
+    uint32_t sub = (uint32_t)__builtin_rintf(tt);
+    uint32_t nrm = min((uint32_t)__float_as_int(ent.y) + (e1 << 3), 0x7eu);
+    keep(sub, nrm);
+    return tt < 8.0f ? sub : nrm;
+}
+
 // Unsigned division by an invariant d (Granlund & Montgomery 1994, Fig. 4.1).
 struct DivMagic {
     uint32_t m, s1, s2;
@@ -395,6 +458,18 @@ __device__ __forceinline__ uint32_t compact_k3(uint32_t w)
     uint32_t y = (x & 0x07070707u) | ((x & 0x70707070u) >> 1);   // 6 bits per byte
     uint32_t z = (y & 0x003f003fu) | ((y & 0x3f003f00u) >> 2);   // 12 bits per half
     return (z & 0x00000fffu) | ((z & 0x0fff0000u) >> 4);
+}
+
+// compact_k2(c0) | compact_k2(c1) << 16: fold within bytes, then one byte
+// permute gathers bytes 0 and 2 of each word.
+__device__ __forceinline__ uint32_t compact_k2_pair(uint32_t c0, uint32_t c1)
+{
+    uint32_t x = c0 & 0x33333333u, y = c1 & 0x33333333u;
+    x = (x | (x >> 2)) & 0x0f0f0f0fu;
+    y = (y | (y >> 2)) & 0x0f0f0f0fu;
+    x |= x >> 4;                                         // bytes 0 and 2 complete
+    y |= y >> 4;
+    return __builtin_amdgcn_perm(y, x, 0x06040200u);
 }
 
 __device__ __forceinline__ uint32_t compact_k1(uint32_t w)
@@ -927,12 +1002,28 @@ __device__ __forceinline__ Outs outs_over(const OnePass &a, uint32_t c0, uint32_
 // Codes, scale byte and guidance bits of this lane's block of one item (raw
 // amax bits ab): one store per plane per lane (8 code bytes, 2k bit-plane
 // bytes, one byte in each scale plane), with no branch.
-template <int K>
-__device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv)
+// Per-group tables (kTab): the block-scale table of block_scale_tab with its
+// offset k, and 1 / (s * g) per scale code.
+struct GroupTabs {
+    const float2 *scale;
+    const float *inv;
+    int k;
+};
+
+template <int K, bool kTab>
+__device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv,
+                                            const GroupTabs &tb)
 {
     const uint32_t cb = w.first - o.c0 + 2 * block_of_lane();   // the block's first chunk, in o's span
-    const uint32_t sc = block_scale(as_f(ab << 16), gv);
-    const float inv = inv_combined(e4m3_decode(sc), gv);
+    uint32_t sc;
+    float inv;
+    if constexpr (kTab) {
+        sc = block_scale_tab(ab, tb.scale, tb.k);
+        inv = tb.inv[sc];
+    } else {
+        sc = block_scale(as_f(ab << 16), gv);
+        inv = inv_combined(e4m3_decode(sc), gv);
+    }
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.scales, cb / 2, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.gds, cb / 2, 0, 0);
     const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
@@ -945,7 +1036,7 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((lo >> 16) | (hi << 8)), o.bits, cb * 3u + 2u, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hi >> 8), o.bits, cb * 3u + 4u, 0, 0);
     } else if (K == 2)
-        __builtin_amdgcn_raw_buffer_store_b32(compact_k2(c0) | (compact_k2(c1) << 16), o.bits, cb * 2u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(compact_k2_pair(c0, c1), o.bits, cb * 2u, 0, 0);
     else
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(compact_k1(c0) | (compact_k1(c1) << 8)), o.bits, cb, 0, 0);
 }
@@ -958,6 +1049,9 @@ __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const 
 // second and takes the even lane's second), so each lane stores chunks t and
 // T + t of the item: 16 B (bf16) or 32 B (f32) per chunk, contiguous across
 // the wave.
+// (The scale tables of quant_block are not used here: this phase is bound by
+// its 4 bytes of stores per element, and timed on gfx950 the two dependent
+// table reads per block cost more than the divisions they replace.)
 template <int OUT>
 __device__ __forceinline__ void rtn_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv)
 {
@@ -1034,6 +1128,8 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     __shared__ int passed;
     __shared__ bool leaving_last;
     __shared__ float gslot[kOpGroupSlots];
+    __shared__ float2 stab[kOneGroup && OUT == 0 ? 256 : 1];   // block-scale table of the one group
+    __shared__ float ctab[kOneGroup && OUT == 0 ? 128 : 1];    // 1 / (s * g) per scale code
 
     const uint32_t P = gridDim.x;
     const uint32_t i0 = (uint32_t)((uint64_t)a.items * blockIdx.x / P);
@@ -1147,6 +1243,19 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     for (uint32_t i = threadIdx.x; i < g_count; i += kOpThreads)
         gslot[i] = as_f(group_amax_bits(a, g_first + i)) / 2688.0f;
     __syncthreads();
+    // One group, rollout codes: its scale tables, from the global scale just read.
+    GroupTabs tabs{stab, ctab, 0};
+    if constexpr (kOneGroup && OUT == 0) {
+        const float g0 = gslot[0];
+        const uint32_t t = threadIdx.x;
+        if (t < 256u) {
+            stab[t] = scale_table_entry(t, g0);
+        } else if (t < 384u) {
+            ctab[t - 256u] = inv_combined(e4m3_decode(t - 256u), g0);
+        }
+        tabs.k = scale_table_k(g0);
+        __syncthreads();
+    }
 
     // ---- phase 2: quantise ------------------------------------------------
     // Item positions are recomputed from a copy the compiler cannot see
@@ -1186,7 +1295,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     };
     auto block_out = [&](const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv) {
         if constexpr (OUT == 0)
-            quant_block<K>(o, w, b, ab, gv);
+            quant_block<K, kOneGroup>(o, w, b, ab, gv, tabs);
         else
             rtn_block<OUT>(o, w, b, ab, gv);
     };
@@ -1725,8 +1834,9 @@ int onepass_device(OnePassDevice &out)
             hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
             hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
             return;
-        // static LDS of the kernel (under 1 KiB) sits below the dynamic tiles
-        d.lds_tiles = lds > 1024 ? (uint32_t)((lds - 1024) / (kOpTile * 16)) : 0u;
+        // static LDS of the kernel (under 4 KiB: the group-scale slots and,
+        // for one group, its scale tables) sits below the dynamic tiles
+        d.lds_tiles = lds > 4096 ? (uint32_t)((lds - 4096) / (kOpTile * 16)) : 0u;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_quant_onepass<2, true, true>, kOpThreads,
                                                          (size_t)d.lds_tiles * kOpTile * 16) != hipSuccess)
             return;
