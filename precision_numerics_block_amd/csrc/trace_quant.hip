@@ -528,9 +528,12 @@ __device__ __forceinline__ float decide(const Entry *tab, float v, uint32_t row,
     float a = fabsf(v);
     float c = __builtin_amdgcn_fmed3f(a, 0.2f, 6.0f);   // bucket clamp
     uint32_t slot = (as_u(c) >> 22) & 15u;
-    Entry e = tab[slot * R + row];
-    bool up = allow && (a > as_f(e.thr));
-    float val = as_f(pick_half(e.vals, up));
+    // One 8-byte LDS read for the whole entry, and no short-circuit: with
+    // `allow && ...` the compiler moved the threshold's read into a branch on
+    // `allow`, one divergent branch and one waited LDS round trip per element.
+    const u32x2 e = reinterpret_cast<const u32x2 *>(tab)[slot * R + row];
+    bool up = (a > as_f(e.x)) & allow;
+    float val = as_f(pick_half(e.y, up));
     float y = (val * s) * g;
     if (kCodes)
         nib = (floor_index_of_slot(slot) + (up ? 1u : 0u)) | ((as_u(v) >> 28) & 8u);
