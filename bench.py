@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     p.add_argument("--k", type=int, default=2, choices=[1, 2, 3], help="guidance bits of the compact stream")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the other guidance widths' and the MXFP4 variant's kernel lines")
+                   help="skip the other guidance widths', the MXFP4 variant's and the FP4 weight kernel lines")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-transport", action="store_true", help="skip the guidance-transport measurements")
     p.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a graph")
@@ -183,6 +183,43 @@ def variant_stats(tq, sets, bufs, ns, Gs, K, k_main):
         lines["guidance_bits_per_element"] = round(8 * tq.guidance_bytes(ns[0], k) / ns[0], 4)
         lines["mismatch_guided"] = round(bad / tot, 6)
         out[f"k{k}"] = lines
+    return out
+
+
+def weight_stats(tq, K):
+    """FP4 weight quantisation (trace_quant_weight) on 64 x 1024 x 2048 bf16
+    expert weights, one global scale per expert matrix: per-kernel burst
+    timing of its amax and its RTN quantiser (no guidance), and the whole
+    call.  Algorithmic bytes read the weights once: 2 + 0.5 + 1/16 B per
+    element."""
+    import torch
+    from precision_numerics_block_amd import synth
+
+    dev = "cuda:0"
+    W = synth.make_weights(synth.WEIGHT_SHAPE, dev).reshape(-1)
+    E = synth.WEIGHT_SHAPE[0]
+    n = W.numel()
+    g = torch.empty(E, dtype=torch.float32, device=dev)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+    runs = {"weight_amax": (2.0, lambda: tq.amax(W, E, out=g)),
+            "weight_quant": (2.0 + 0.5 + 1 / 16,
+                             lambda: tq.quant_rollout(W, g, 2, E, guidance=False, codes=codes, scales=scales)),
+            "quant_weight": (2.0 + 0.5 + 1 / 16, lambda: tq.quant_weight(W, E, g=g, codes=codes, scales=scales))}
+    out = {"workload": f"expert weights {'x'.join(map(str, synth.WEIGHT_SHAPE))} bf16, G={E} (one per matrix)"}
+    for nm, (bpe, fn) in runs.items():
+        for _ in range(2):
+            fn()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(e) / K
+        gbs = bpe * n / (ms * 1e-3) / 1e9
+        out[nm] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del W
     return out
 
 
@@ -558,6 +595,7 @@ def main():
         raise RuntimeError(f"device status words report {bad} ({tq.lib.trace_status_str(bad[0]).decode()})")
     variants = None if args.no_variants else variant_stats(tq, sets, bufs, ns, Gs, min(K, 20), k)
     mx = None if args.no_variants else mx_stats(tq, sets, ns, min(K, 20), k)
+    weights = None if args.no_variants else weight_stats(tq, min(K, 20))
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
@@ -604,6 +642,7 @@ def main():
         "kernels": kernels,
         "guidance_widths": variants,
         "mxfp4": mx,
+        "fp4_weight": weights,
         "transport": transport,
     }
     print(json.dumps(out))

@@ -101,6 +101,19 @@ size_t trace_guidance_bytes(int64_t n, int k);
  * Enqueues three small kernels (clear, reduce, finalise). */
 int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_dev, void *stream);
 
+/* FP4 weight quantisation for the rollout's FP4 weight/activation GEMMs
+ * ([en] opening paragraph and [ru] key facts: rollout runs with FP4 weights
+ * and activations plus an FP4 KV cache).  Weights are not guided (rollout and
+ * trainer hold the same weights), so no guidance stream is written.
+ * w_bf16: bf16[n], G matrices of n / G contiguous elements each, blocks of 16
+ * along the contiguous (GEMM reduction) dimension.  g_out: f32[G], written
+ * with amax(|w| over the matrix) / 2688.  codes: u8[n/2]; scales: u8[n/16]
+ * (as trace_quant_rollout).  status_dev: as trace_amax.  Enqueues
+ * trace_amax's kernels, then the RTN quantiser; on an argument error nothing
+ * is enqueued. */
+int trace_quant_weight(const void *w_bf16, int64_t n, int G, float *g_out, uint8_t *codes, uint8_t *scales,
+                       int *status_dev, void *stream);
+
 /* Rollout quantisation with standard RTN ("TRACE Core Concept": the rollout
  * side's actual FP4 result), fused with the guidance emit.
  * y_bf16: bf16[n]; g: f32[G] from trace_amax; k in {1, 2, 3, 4}.

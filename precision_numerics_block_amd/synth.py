@@ -21,6 +21,11 @@ RL Rollouts", section "TRACE Core Concept"):
   5  batched MoE step: activations 128 x 1024 x 4096 Student-t(nu=3) plus K, V
      each 65536 x 8 x 128 (as 3), relative noise 0.01
 
+Weights (the rollout's FP4 weights; not guided, so no rollout copy):
+  W  expert weight matrices E x out x in (64 x 1024 x 2048), blocks along in:
+     W[e] = sigma_e * N(0,1) with sigma_e = 0.02 * exp(0.3 * z_e), z_e ~ N(0,1),
+     and 0.1% of entries x8 (outlier weights); seeds 9000 + role.
+
 "Relative noise r" means Y = bf16(float(X) + r * |float(X)| * Z), Z ~ N(0,1).
 Seeds: one torch.Generator per (workload, tensor, role), seeded with
 1000 * workload + 10 * tensor index + role (0 = X, 1 = noise, 2 = extra).
@@ -29,7 +34,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_pair", "make_workload", "tensor_specs"]
+__all__ = ["Workload", "WORKLOADS", "WEIGHT_SHAPE", "make_pair", "make_weights", "make_workload", "tensor_specs"]
+
+WEIGHT_SHAPE = (64, 1024, 2048)     # experts x out x in
 
 
 @dataclass(frozen=True)
@@ -140,3 +147,12 @@ def make_workload(index, device="cpu", rows=None):
     """{name: (X, Y)} for every tensor of the workload."""
     return {name: make_pair(index, pos, shape, device)
             for pos, (name, shape) in enumerate(tensor_specs(index, rows))}
+
+
+def make_weights(shape=WEIGHT_SHAPE, device="cpu"):
+    """bf16 expert weights E x out x in (workload W above)."""
+    E = shape[0]
+    sigma = 0.02 * torch.exp(0.3 * _normal((E,), device, 9002))
+    w = _normal(shape, device, 9000) * sigma.view(E, *([1] * (len(shape) - 1)))
+    u = torch.rand(shape, generator=_gen(device, 9001), device=device)
+    return torch.where(u < 0.001, w * 8.0, w).to(torch.bfloat16)

@@ -27,6 +27,7 @@ _SIGS = {
     "trace_guidance_bytes": (_sz, [_i64, _int]),
     "trace_amax": (_int, [_vp, _i64, _int, _vp, _vp, _vp]),
     "trace_quant_rollout": (_int, [_vp, _i64, _int, _vp, _int, _vp, _vp, _vp, _vp]),
+    "trace_quant_weight": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "trace_guidance_pack": (_int, [_vp, _vp, _i64, _int, _vp, _vp]),
     "trace_onepass_work_bytes": (_sz, [_int]),
     "trace_onepass_capacity": (_i64, [_int]),
@@ -59,7 +60,7 @@ for _name, (_res, _args) in _SIGS.items():
 OUT_BF16, OUT_F32 = 0, 1
 
 __all__ = [
-    "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout",
+    "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout", "quant_weight",
     "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass", "fakequant_rtn_onepass",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
     "mx_scale_bytes", "mx_guidance_bytes", "mx_quant_rollout", "mx_fakequant_guided", "mx_fakequant_rtn",
@@ -141,6 +142,20 @@ def quant_rollout(y, g, k, G=1, guidance=True, codes=None, scales=None):
     _check("trace_quant_rollout", lib.trace_quant_rollout(
         _ptr(y), n, int(G), _ptr(g), int(k), _ptr(codes), _ptr(scales), _ptr(guidance), _stream(dev)))
     return codes, scales, guidance
+
+
+def quant_weight(w, G=1, g=None, codes=None, scales=None, status=None):
+    """FP4 weights: global scale per matrix (G matrices), RTN codes u8[n/2]
+    and E4M3 block scales u8[n/16] along the contiguous dimension; no
+    guidance.  Returns (g, codes, scales)."""
+    _need(w, torch.bfloat16, "w")
+    n, dev = w.numel(), w.device
+    g = torch.empty(G, dtype=torch.float32, device=dev) if g is None else g
+    codes = _u8(n // 2, dev) if codes is None else codes
+    scales = _u8(n // 16, dev) if scales is None else scales
+    _check("trace_quant_weight", lib.trace_quant_weight(
+        _ptr(w), n, int(G), _ptr(g), _ptr(codes), _ptr(scales), _ptr(status), _stream(dev)))
+    return g, codes, scales
 
 
 def onepass_work_bytes(G=1):

@@ -89,6 +89,17 @@ def test_argument_errors_before_any_hip_call(tq):
     assert L.trace_fakequant_guided(A, n, 1, A, A, 4, A, 0, None, None) == E_K
     assert L.trace_fakequant_guided(A, n, 1, A, A, 2, A, 7, None, None) == E_DTYPE
     assert L.trace_fakequant_rtn(A, n, 1, A, None, A, 2, None, None, None) == E_DTYPE
+    # weight quantisation: its own checks come before the amax it enqueues
+    qw = L.trace_quant_weight
+    assert qw(A, 24, 1, A, A, A, None, None) == E_SIZE
+    assert qw(A, n, 3, A, A, A, None, None) == E_SIZE
+    assert qw(None, n, 1, A, A, A, None, None) == E_NULL
+    assert qw(A, n, 1, None, A, A, None, None) == E_NULL
+    assert qw(A, n, 1, A, None, A, None, None) == E_NULL
+    assert qw(A, n, 1, A, A, None, None, None) == E_NULL
+    assert qw(A, n, 1, A, A + 8, A, None, None) == E_ALIGN
+    assert qw(A, n, 1, A, A, A + 4, None, None) == E_ALIGN
+    assert qw(A, n, 1, A, A, A, A + 4, None) == E_ALIGN
     # one-pass rollout: every argument error is found before the device query
     op = L.trace_quant_rollout_onepass
     assert op(A, 24, 1, 2, A, A, A, None, A, 0, None, None) == E_SIZE
