@@ -605,10 +605,11 @@ def test_onepass_nonfinite_flag_and_repeat(tq):
     assert bool((work == 0).all()), "the call leaves its work buffer zeroed"
     og, _ = oracle.amax(h16(X))
     assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
-    # the same work buffer again, several calls with other sizes, groups and
-    # workgroup caps: each call finds it zeroed by the previous one
+    # the same work buffer again, several calls with other sizes, group
+    # counts (up, down and up again) and workgroup caps: each call finds it
+    # zeroed by the previous one
     X2, Y2 = synth.make_pair(1, 0, (256, 2048), DEV)
-    for G, cap in ((1, 0), (2, 0), (1, 3), (2, 5), (1, 0)):
+    for G, cap in ((1, 0), (2, 0), (1, 3), (2, 5), (1, 0), (8, 0), (1, 0), (8, 2), (4, 0), (8, 0)):
         st.zero_()
         g2, c2, s2, gd2 = tq.quant_rollout_onepass(Y2, 2, G, status=st, work=work, max_workgroups=cap)
         torch.cuda.synchronize()
@@ -776,6 +777,17 @@ def test_rtn_onepass_graph_replay_and_work_reuse(tq):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(g, ref_g), rep
+        assert bool((work == 0).all())
+    # the same buffer alternating with the one-pass rollout (same layout)
+    _, Y = synth.make_pair(2, 0, (4, 512, 2048), DEV)
+    gy = tq.amax(Y)
+    cy, sy, dy = tq.quant_rollout(Y, gy, 2)
+    for rep in range(3):
+        g1, c1, s1, d1 = tq.quant_rollout_onepass(Y, 2, work=work)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g1, gy) and torch.equal(c1, cy) and torch.equal(s1, sy) and torch.equal(d1, dy), rep
         assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)) and torch.equal(g, ref_g), rep
         assert bool((work == 0).all())
 
