@@ -36,6 +36,7 @@
 #include <cfloat>
 #include <cstdint>
 #include <cstdlib>
+#include <algorithm>
 #include <mutex>
 
 #include "trace_quant.h"
@@ -837,11 +838,13 @@ constexpr uint32_t kOpTopWord = kOpSubgroups * kOpLine;
 constexpr uint32_t kOpDoneWord = (kOpSubgroups + 1) * kOpLine;      // the same tree again, for departures
 constexpr uint32_t kOpAccWord = 2 * (kOpSubgroups + 1) * kOpLine;
 constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
+constexpr uint32_t kOpTabSlots = 4;                // groups with scale tables, several-group rollout
 
 struct OnePass {
     const u32x4 *y;         // the input (the rollout's y, or the training tensor x)
     uint32_t cpg;           // chunks per group
     uint32_t tpg;           // tiles per group
+    DivMagic tpg_div;       // division by tpg (item -> group), a multiply-high on the scalar unit
     uint32_t items;         // G * tpg
     uint32_t G;
     uint32_t lds_tiles;     // tiles a workgroup keeps in LDS
@@ -866,7 +869,7 @@ struct Item {
 template <bool kOneGroup>
 __device__ __forceinline__ Item item_at(const OnePass &a, uint32_t it)
 {
-    uint32_t grp = kOneGroup ? 0u : it / a.tpg;
+    uint32_t grp = kOneGroup ? 0u : div_magic(it, a.tpg_div);
     uint32_t tile = it - grp * a.tpg;
     uint32_t off = tile * kOpTile;
     return Item{grp, grp * a.cpg + off, min(a.cpg - off, (uint32_t)kOpTile)};
@@ -1132,16 +1135,22 @@ __device__ __forceinline__ bool tree_count(uint32_t *base, uint32_t P, bool *top
 // kSpan: output descriptors over the workgroup's whole run (see Outs).
 // OUT: 0 = rollout (codes, scales, guidance of width K); 1 / 2 = plain RTN
 // fake-quant with own block scales, output bf16 / f32 (K unused).
-template <int K, bool kOneGroup, bool kSpan, int OUT = 0>
+// kTab (rollout only): scale tables per group (block_scale_tab); with
+// several groups the host launches it only when no workgroup's run spans
+// more than kOpTabSlots groups.
+template <int K, bool kOneGroup, bool kSpan, int OUT = 0, bool kTab = kOneGroup && OUT == 0>
 __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
 {
+    static_assert(!kTab || OUT == 0, "scale tables serve the rollout codes only");
+    constexpr uint32_t kSlots = kTab ? (kOneGroup ? 1u : kOpTabSlots) : 0u;
     extern __shared__ u32x4 lds_tiles[];           // a.lds_tiles * 2 * kOpThreads chunks
     __shared__ uint32_t wmax[kOpThreads / 64];
     __shared__ int passed;
     __shared__ bool leaving_last;
     __shared__ float gslot[kOpGroupSlots];
-    __shared__ float2 stab[kOneGroup && OUT == 0 ? 256 : 1];   // block-scale table of the one group
-    __shared__ float ctab[kOneGroup && OUT == 0 ? 128 : 1];    // 1 / (s * g) per scale code
+    __shared__ float2 stab[kTab ? kSlots * 256 : 1];   // block-scale table per group slot
+    __shared__ float ctab[kTab ? kSlots * 128 : 1];    // 1 / (s * g) per scale code, per slot
+    __shared__ int ktab[kTab ? kSlots : 1];
 
     const uint32_t P = gridDim.x;
     const uint32_t i0 = (uint32_t)((uint64_t)a.items * blockIdx.x / P);
@@ -1256,18 +1265,26 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
         gslot[i] = as_f(group_amax_bits(a, g_first + i)) / 2688.0f;
     __syncthreads();
     // One group, rollout codes: its scale tables, from the global scale just read.
-    GroupTabs tabs{stab, ctab, 0};
-    if constexpr (kOneGroup && OUT == 0) {
-        const float g0 = gslot[0];
-        const uint32_t t = threadIdx.x;
-        if (t < 256u) {
-            stab[t] = scale_table_entry(t, g0);
-        } else if (t < 384u) {
-            ctab[t - 256u] = inv_combined(e4m3_decode(t - 256u), g0);
+    if constexpr (kTab) {
+        const uint32_t ns = min(g_count, kSlots);
+        for (uint32_t i = threadIdx.x; i < ns * 384u; i += kOpThreads) {
+            const uint32_t sl = i / 384u, e = i - sl * 384u;
+            const float gs = gslot[sl];
+            if (e < 256u)
+                stab[sl * 256u + e] = scale_table_entry(e, gs);
+            else
+                ctab[sl * 128u + e - 256u] = inv_combined(e4m3_decode(e - 256u), gs);
         }
-        tabs.k = scale_table_k(g0);
+        if (threadIdx.x < ns)
+            ktab[threadIdx.x] = scale_table_k(gslot[threadIdx.x]);
         __syncthreads();
     }
+    // The tables of an item's group (slot = group - g_first, below kSlots by
+    // the host's choice; clamped so that a slip cannot leave the arrays).
+    auto tabs_for = [&](uint32_t grp) {
+        const uint32_t sl = kOneGroup ? 0u : min(grp - g_first, kSlots > 0 ? kSlots - 1 : 0u);
+        return GroupTabs{stab + sl * 256u, ctab + sl * 128u, kTab ? ktab[sl] : 0};
+    };
 
     // ---- phase 2: quantise ------------------------------------------------
     // Item positions are recomputed from a copy the compiler cannot see
@@ -1305,9 +1322,11 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
             return none;
         return kSpan ? span : outs_over<K, OUT>(a, w.first, w.count);
     };
+    // (gv: the item's global scale; with scale tables it is not needed, and
+    // not fetched, since the fetch past the LDS slots is a device-scope load)
     auto block_out = [&](const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv) {
         if constexpr (OUT == 0)
-            quant_block<K, kOneGroup>(o, w, b, ab, gv, tabs);
+            quant_block<K, kTab>(o, w, b, ab, gv, tabs_for(w.grp));
         else
             rtn_block<OUT>(o, w, b, ab, gv);
     };
@@ -1317,12 +1336,12 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     for (int h = 0; h < kOpRegTiles; ++h) {
         Item w = item_at<kOneGroup>(a, p2_reg + h);
         bool live = p2_reg + h < i0 + cnt;
-        block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live ? gscale(w.grp) : 0.0f);
+        block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live && !kTab ? gscale(w.grp) : 0.0f);
     }
     for (uint32_t j = 0; j < nlds; ++j) {
         Item w = item_at<kOneGroup>(a, p2_lds + j);
         Blk b = block_from_lds(lds_tiles, j);
-        block_out(outs_for(w, true), w, b, block_amax_bits(b), gscale(w.grp));
+        block_out(outs_for(w, true), w, b, block_amax_bits(b), kTab ? 0.0f : gscale(w.grp));
     }
     for (uint32_t j = 0; j < nstr; j += kOpStream) {
         Chunk x[kOpStream][2];
@@ -1334,7 +1353,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
         for (int q = 0; q < kOpStream; ++q) {
             bool live = j + q < nstr;
             Blk b = to_block(x[q]);
-            block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live ? gscale(w[q].grp) : 0.0f);
+            block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live && !kTab ? gscale(w[q].grp) : 0.0f);
         }
     }
 
@@ -1846,10 +1865,11 @@ int onepass_device(OnePassDevice &out)
             hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
             hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
             return;
-        // static LDS of the kernel (under 4 KiB: the group-scale slots and,
-        // for one group, its scale tables) sits below the dynamic tiles
-        d.lds_tiles = lds > 4096 ? (uint32_t)((lds - 4096) / (kOpTile * 16)) : 0u;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_quant_onepass<2, true, true>, kOpThreads,
+        // static LDS of the kernel (under 12 KiB: the group-scale slots and
+        // the scale tables of up to kOpTabSlots groups) sits below the
+        // dynamic tiles; occupancy is taken for the variant with the most
+        d.lds_tiles = lds > 12288 ? (uint32_t)((lds - 12288) / (kOpTile * 16)) : 0u;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_quant_onepass<2, false, true, 0, true>, kOpThreads,
                                                          (size_t)d.lds_tiles * kOpTile * 16) != hipSuccess)
             return;
         d.per_cu = per;
@@ -1903,6 +1923,7 @@ int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work
     a.y = (const u32x4 *)in_bf16;
     a.cpg = nchunk / (uint32_t)G;
     a.tpg = (a.cpg + kOpTile - 1) / kOpTile;
+    a.tpg_div = make_div_magic(a.tpg);
     a.items = a.tpg * (uint32_t)G;                       // <= nchunk / 2 + G < 2^32
     a.G = (uint32_t)G;
     a.lds_tiles = d.lds_tiles;
@@ -1960,11 +1981,25 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     (void)hipGetLastError();
 #define TRACE_OP(KK, ONE, SPAN) \
     hipLaunchKernelGGL((k_quant_onepass<KK, ONE, SPAN>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
+#define TRACE_OPT(KK) \
+    hipLaunchKernelGGL((k_quant_onepass<KK, false, true, 0, true>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
+    // the most groups one workgroup's run of items spans (runs as in the kernel)
+    uint32_t span = 0;
+    for (int64_t b = 0; b < grid; ++b) {
+        uint32_t f = (uint32_t)((uint64_t)a.items * (uint64_t)b / (uint64_t)grid);
+        uint32_t l = (uint32_t)((uint64_t)a.items * (uint64_t)(b + 1) / (uint64_t)grid) - 1u;
+        span = std::max(span, l / a.tpg - f / a.tpg + 1u);
+    }
     if (G == 1) {                                      // one group: only the tensor's last tile can be short
         if (k == 1) TRACE_OP(1, true, true);
         else if (k == 2) TRACE_OP(2, true, true);
         else if (k == 3) TRACE_OP(3, true, true);
         else TRACE_OP(4, true, true);
+    } else if (a.cpg % kOpTile == 0 && span <= kOpTabSlots) {   // whole tiles, scale tables for every run
+        if (k == 1) TRACE_OPT(1);
+        else if (k == 2) TRACE_OPT(2);
+        else if (k == 3) TRACE_OPT(3);
+        else TRACE_OPT(4);
     } else if (a.cpg % kOpTile == 0) {                 // groups of whole tiles
         if (k == 1) TRACE_OP(1, false, true);
         else if (k == 2) TRACE_OP(2, false, true);
@@ -1977,6 +2012,7 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
         else TRACE_OP(4, false, false);
     }
 #undef TRACE_OP
+#undef TRACE_OPT
     return launched();
 }
 

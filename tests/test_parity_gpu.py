@@ -528,6 +528,19 @@ def test_onepass_small_full_parity(tq, wl, rows, ti, caps):
                 c.check()
 
 
+@pytest.mark.parametrize("G,cap", [(2, 0), (4, 1), (8, 1), (8, 2), (16, 3), (64, 0), (64, 5)])
+def test_onepass_group_scale_tables(tq, G, cap):
+    """Groups of whole tiles (256 x 2048, 64 tiles): with no workgroup run
+    spanning more than four groups the rollout uses per-group scale tables,
+    otherwise the per-block divisions; both against the oracle (G, cap pairs
+    chosen to land on each side: 8 groups with one workgroup spans 8)."""
+    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
+    for k in (2, 3):
+        c = Checker(tq, X, Y, k, G, onepass=cap)
+        c.run_gpu(out_f32=False)
+        c.check()
+
+
 ONEPASS_FULL = [(2, 0, 1), (2, 0, 64), (3, 0, 1), (4, 0, 1), (5, 0, 1), (5, 1, 1)]
 
 
