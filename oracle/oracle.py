@@ -31,11 +31,15 @@ _lib = None
 
 
 def lib():
+    """Load the oracle library.  TRACE_ORACLE_LIB names another build of
+    ``trace_oracle.c`` to load instead (the pins' mutation test uses it to run
+    the pins against copies with planted mistakes)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("TRACE_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         i64, i32, f32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
         vp, u8 = ctypes.c_void_p, ctypes.c_uint8
         sig = {
