@@ -6,11 +6,12 @@ tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
 0.01, k = 2 guidance bits):
 
   rollout   amax(Y) + RTN quantise + guidance (k): the one-pass kernel (one
-            read of Y) when the tensor fits on chip, else amax(Y) then the
-            quantise kernel (--rollout picks either); full-code pack (k = 4)
+            read of Y) when one global-scale group fits on chip (one launch
+            per block of groups that fits), else amax(Y) then the quantise
+            kernel (--rollout picks either); full-code pack (k = 4)
   training  guided fake-quant (k) -> full-code fake-quant -> plain QAT:
-            amax(X) + RTN fake-quant with own scales (one-pass kernel when the
-            tensor fits on chip, else the two kernels)
+            amax(X) + RTN fake-quant with own scales (one-pass kernel when a
+            group fits on chip, else the two kernels)
 
 `value` is the whole step's algorithmic bytes per second (GB/s) over K timed
 steps, replayed from a HIP graph.  Algorithmic bytes: every operation of the
@@ -459,10 +460,11 @@ def main():
         )
 
     bufs = [[make_bufs(shape, n, G) for shape, n, G in zip(shapes, ns, Gs)] for _ in range(2)]
-    # rollout path per tensor: one-pass when the tensor (in whole tiles of
-    # 8192 elements per group) fits on chip
+    # rollout path per tensor: one-pass when one group (in whole tiles of 8192
+    # elements) fits on chip; the library runs one launch per block of whole
+    # groups that fits when the tensor as a whole does not
     cap = tq.onepass_capacity()
-    fits = [G * -(-(n // G) // 8192) * 8192 <= cap for n, G in zip(ns, Gs)]
+    fits = [-(-(n // G) // 8192) * 8192 <= cap for n, G in zip(ns, Gs)]
     onepass = [args.rollout == "onepass" or (args.rollout == "auto" and f) for f in fits]
 
     def qat_rtn(X, b, G, one):

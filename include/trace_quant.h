@@ -126,12 +126,15 @@ int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, in
  * rounded up to a multiple of 256 (0 if G < 1). */
 size_t trace_onepass_work_bytes(int G);
 
-/* Elements the one-pass rollout keeps on chip on the current device with at
- * most max_workgroups workgroups (0 = one per compute unit): tensors up to
- * this size (with G > 1, each group counted in whole tiles of 8192 elements)
- * are read once; beyond it the excess is read twice and the two-kernel path
- * (trace_amax + trace_quant_rollout) is usually faster.  0 on error (no
- * device, max_workgroups < 0). */
+/* Elements the one-pass rollout keeps on chip in one launch on the current
+ * device with at most max_workgroups workgroups (0 = one per compute unit):
+ * tensors up to this size (with G > 1, each group counted in whole tiles of
+ * 8192 elements) are one launch that reads the input once.  A larger tensor
+ * with G > 1 whose groups each fit runs one launch per block of whole groups
+ * that fits, and is still read once.  Otherwise (G = 1, or a group larger
+ * than this) the excess is read twice and the two-kernel path (trace_amax +
+ * trace_quant_rollout) is usually faster.  0 on error (no device,
+ * max_workgroups < 0). */
 int64_t trace_onepass_capacity(int max_workgroups);
 
 /* One-pass rollout: the results of trace_amax followed by trace_quant_rollout
@@ -156,7 +159,10 @@ int64_t trace_onepass_capacity(int max_workgroups);
  * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s; the
  * environment variable TRACE_ONEPASS_WAIT_US, read at each call, replaces it,
  * which lets a test force the failure path); the outputs are then undefined.
- * Enqueues one kernel. */
+ * Enqueues one kernel, or one per block of groups when the tensor exceeds
+ * trace_onepass_capacity and its groups fit (see there); every launch writes
+ * its groups' parts of the same output planes and leaves the work buffer
+ * zeroed for the next. */
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);
@@ -169,7 +175,8 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
  * unstable baseline; "Why Does FP4 Rollout 'Break' RL Training?": RTN with
  * a global and a block scale.  g_out: f32[G], written; y_out: bf16[n] or
  * f32[n] per out_dtype; codes_out (u8[n/2]) and scales_out (u8[n/16]) are
- * nullable.  Enqueues one kernel. */
+ * nullable.  Enqueues one kernel, or one per block of groups as
+ * trace_quant_rollout_onepass does. */
 int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
                                 uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups,
                                 int *status_dev, void *stream);

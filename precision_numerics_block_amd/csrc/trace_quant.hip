@@ -1948,36 +1948,53 @@ int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work
     return TRACE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
-                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
-                                int *status_dev, void *stream)
+// Groups per launch of the one-pass entry points.  A tensor that fits on chip
+// is one launch.  With several groups, when the whole tensor does not fit but
+// one group does, the call runs one launch per block of whole groups that
+// fits (as few blocks as possible, of equal size but the last): each launch
+// reads its part once, and groups share nothing, so the results are those of
+// one launch.  Otherwise (one group, or a group larger than the chip) one
+// launch reads the excess twice.
+int onepass_groups_per_launch(int64_t n, int G, int max_workgroups, int &gpb)
 {
-    int rc = check_sizes(n, G);
-    if (rc)
+    OnePassDevice d;
+    int rc = onepass_device(d);
+    if (rc != TRACE_OK)
         return rc;
-    if (!y_bf16 || !g_out || !codes || !scales || !work)
-        return TRACE_E_NULL;
-    if (!aligned16(y_bf16) || !aligned16(g_out) || !aligned16(codes) || !aligned16(scales) ||
-        (guidance && !aligned16(guidance)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
-        return TRACE_E_ALIGN;
-    if (k < 1 || k > 4)
-        return TRACE_E_K;
-    if (max_workgroups < 0)
-        return TRACE_E_SIZE;
+    int64_t grid = (int64_t)d.cus * d.per_cu;
+    if (max_workgroups > 0 && max_workgroups < grid)
+        grid = max_workgroups;
+    const int64_t cap_tiles = grid * (int64_t)(kOpRegTiles + d.lds_tiles);
+    const int64_t tpg = (n / 8 / G + kOpTile - 1) / kOpTile;
+    gpb = G;
+    if (G > 1 && tpg * G > cap_tiles && tpg <= cap_tiles) {
+        const int64_t fit = cap_tiles / tpg;
+        const int64_t blocks = (G + fit - 1) / fit;
+        gpb = (int)((G + blocks - 1) / blocks);
+    }
+    return TRACE_OK;
+}
+
+// One launch of the one-pass rollout over n elements in G groups, with the
+// outputs at the given places (a block of groups of a larger tensor writes
+// into that tensor's planes); the guidance pad [pad_begin, pad_end) is
+// relative to gd_scales.
+int rollout_onepass_launch(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                           uint8_t *scales, uint8_t *gd_scales, uint8_t *gd_bits, uint32_t pad_begin,
+                           uint32_t pad_end, void *work, int max_workgroups, int *status_dev, hipStream_t st)
+{
     OnePass a;
     int64_t grid;
     size_t lds;
-    if ((rc = onepass_plan(y_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds)) != TRACE_OK)
+    int rc = onepass_plan(y_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds);
+    if (rc != TRACE_OK)
         return rc;
     a.codes = (uint32_t *)codes;
     a.scales = scales;
-    a.gd_scales = guidance;
-    a.gd_bits = guidance ? guidance + bitplane_offset(n) : nullptr;
-    hipStream_t st = (hipStream_t)stream;
+    a.gd_scales = gd_scales;
+    a.gd_bits = gd_bits;
+    a.pad_begin = pad_begin;
+    a.pad_end = pad_end;
     (void)hipGetLastError();
 #define TRACE_OP(KK, ONE, SPAN) \
     hipLaunchKernelGGL((k_quant_onepass<KK, ONE, SPAN>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
@@ -2016,32 +2033,20 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     return launched();
 }
 
-int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
-                                uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups,
-                                int *status_dev, void *stream)
+// One launch of the one-pass own-scale RTN fake-quant (as above).
+int rtn_onepass_launch(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, bool f32,
+                       uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups, int *status_dev,
+                       hipStream_t st)
 {
-    int rc = check_sizes(n, G);
-    if (rc)
-        return rc;
-    if (!x_bf16 || !g_out || !y_out || !work)
-        return TRACE_E_NULL;
-    if (!aligned16(x_bf16) || !aligned16(g_out) || !aligned16(y_out) || (codes_out && !aligned16(codes_out)) ||
-        (scales_out && !aligned16(scales_out)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
-        return TRACE_E_ALIGN;
-    if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
-        return TRACE_E_DTYPE;
-    if (max_workgroups < 0)
-        return TRACE_E_SIZE;
     OnePass a;
     int64_t grid;
     size_t lds;
-    if ((rc = onepass_plan(x_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds)) != TRACE_OK)
+    int rc = onepass_plan(x_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds);
+    if (rc != TRACE_OK)
         return rc;
     a.codes = (uint32_t *)codes_out;
     a.scales = scales_out;
     a.out = y_out;
-    hipStream_t st = (hipStream_t)stream;
-    bool f32 = out_dtype == TRACE_OUT_F32;
     (void)hipGetLastError();
 #define TRACE_OR(ONE, SPAN)                                                                                        \
     do {                                                                                                           \
@@ -2058,6 +2063,78 @@ int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_o
         TRACE_OR(false, false);
 #undef TRACE_OR
     return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
+                                int *status_dev, void *stream)
+{
+    int rc = check_sizes(n, G);
+    if (rc)
+        return rc;
+    if (!y_bf16 || !g_out || !codes || !scales || !work)
+        return TRACE_E_NULL;
+    if (!aligned16(y_bf16) || !aligned16(g_out) || !aligned16(codes) || !aligned16(scales) ||
+        (guidance && !aligned16(guidance)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
+        return TRACE_E_ALIGN;
+    if (k < 1 || k > 4)
+        return TRACE_E_K;
+    if (max_workgroups < 0)
+        return TRACE_E_SIZE;
+    int gpb;
+    if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
+        return rc;
+    const int64_t per = n / G, bits = bitplane_offset(n);
+    for (int g0 = 0; g0 < G; g0 += gpb) {              // blocks of whole groups (one block when it all fits)
+        const int gb = std::min(gpb, G - g0);
+        const int64_t e0 = (int64_t)g0 * per;          // a multiple of 16: every plane's offset is whole bytes
+        rc = rollout_onepass_launch(static_cast<const uint16_t *>(y_bf16) + e0, gb * per, gb, k, g_out + g0,
+                                    codes + e0 / 2, scales + e0 / 16, guidance ? guidance + e0 / 16 : nullptr,
+                                    guidance ? guidance + bits + e0 * k / 8 : nullptr,
+                                    g0 == 0 ? (uint32_t)(n / 16) : 0u, g0 == 0 ? (uint32_t)bits : 0u, work,
+                                    max_workgroups, status_dev, (hipStream_t)stream);
+        if (rc != TRACE_OK)
+            return rc;
+    }
+    return TRACE_OK;
+}
+
+int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
+                                uint8_t *codes_out, uint8_t *scales_out, void *work, int max_workgroups,
+                                int *status_dev, void *stream)
+{
+    int rc = check_sizes(n, G);
+    if (rc)
+        return rc;
+    if (!x_bf16 || !g_out || !y_out || !work)
+        return TRACE_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(g_out) || !aligned16(y_out) || (codes_out && !aligned16(codes_out)) ||
+        (scales_out && !aligned16(scales_out)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
+        return TRACE_E_ALIGN;
+    if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
+        return TRACE_E_DTYPE;
+    if (max_workgroups < 0)
+        return TRACE_E_SIZE;
+    int gpb;
+    if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
+        return rc;
+    const bool f32 = out_dtype == TRACE_OUT_F32;
+    const int64_t per = n / G;
+    for (int g0 = 0; g0 < G; g0 += gpb) {              // blocks of whole groups (one block when it all fits)
+        const int gb = std::min(gpb, G - g0);
+        const int64_t e0 = (int64_t)g0 * per;
+        rc = rtn_onepass_launch(static_cast<const uint16_t *>(x_bf16) + e0, gb * per, gb, g_out + g0,
+                                static_cast<uint8_t *>(y_out) + e0 * (f32 ? 4 : 2), f32,
+                                codes_out ? codes_out + e0 / 2 : nullptr, scales_out ? scales_out + e0 / 16 : nullptr,
+                                work, max_workgroups, status_dev, (hipStream_t)stream);
+        if (rc != TRACE_OK)
+            return rc;
+    }
+    return TRACE_OK;
 }
 
 size_t trace_code_bytes(int64_t n) { return check_sizes(n, 1) ? 0 : (size_t)(n / 2); }

@@ -571,6 +571,77 @@ def test_onepass_full_size_sampled(tq, wl, ti, G):
     torch.cuda.empty_cache()
 
 
+# Tensors beyond the on-chip capacity with several groups: when one group
+# fits, the one-pass entry points run one launch per block of whole groups,
+# writing into the whole tensor's planes; when a group is larger than the
+# chip, one launch reads the excess twice.  Outputs start as a canary so that
+# every byte must come from a launch.  (tensor, size, G, workgroup cap, ks):
+# "act" = size x 512 x 2048 activations (128 tiles of 8192 per row); "ragged"
+# = size blocks of random data, groups ending mid-tile.
+GROUP_BLOCKS = [
+    ("act", 2, 4, 1, (2,)),              # 64-tile groups, 33 tiles on chip: excess read twice
+    ("act", 2, 2, 3, (2,)),              # 128-tile groups, 99 on chip: excess read twice
+    ("act", 2, 4, 2, (1, 2, 3, 4)),      # 66 on chip: 4 launches of one group
+    ("act", 2, 4, 5, (1, 2, 3, 4)),      # 165 on chip: 2 launches of two groups
+    ("act", 2, 8, 3, (1, 2, 3, 4)),      # 32-tile groups, 99 on chip: launches of 3, 3 and 2 groups
+    ("ragged", 3 * 7001, 3, 1, (1, 2, 3, 4)),   # 14-tile groups (last tile short): launches of 2 and 1
+]
+
+
+def _group_blocks_pair(kind, size):
+    if kind == "act":
+        return synth.make_pair(2, 0, (size, 512, 2048), DEV)
+    rng = np.random.default_rng(size)
+    x = rng.standard_normal(16 * size) * np.exp(rng.uniform(-3, 3, 16 * size))
+    return _pair_from_np(x, 0.01, size)
+
+
+def _canary(n, dtype=torch.uint8):
+    return torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV).view(dtype)
+
+
+@pytest.mark.parametrize("kind,size,G,cap,ks", GROUP_BLOCKS)
+def test_onepass_group_blocks(tq, kind, size, G, cap, ks):
+    X, Y = _group_blocks_pair(kind, size)
+    n = X.numel()
+    group_tiles = -(-(n // G // 8) // 1024)
+    cap_tiles = tq.onepass_capacity(cap) // 8192
+    assert G * group_tiles > cap_tiles, "the case must exceed the on-chip capacity"
+    Xh, Yh = h16(X), h16(Y)
+    gY, _ = oracle.amax(Yh, G)
+    gX, _ = oracle.amax(Xh, G)
+    for k in ks:
+        g = torch.full((G,), -1.0, device=DEV)
+        codes, scales, gd = _canary(n // 2), _canary(n // 16), _canary(tq.guidance_bytes(n, k))
+        st = torch.zeros(4, dtype=torch.int32, device=DEV)
+        tq.quant_rollout_onepass(Y, k, G, g=g, guidance=gd, codes=codes, scales=scales, max_workgroups=cap,
+                                 status=st)
+        torch.cuda.synchronize()
+        assert int(st[0]) == 0
+        oc, os_, ogd = oracle.quant_rollout(Yh, gY, k, G)
+        assert_eq(g.cpu().numpy().view(np.uint32), gY.view(np.uint32), f"k={k} global scales")
+        assert_eq(h8(codes), oc, f"k={k} codes")
+        assert_eq(h8(scales), os_, f"k={k} scales")
+        assert_eq(h8(gd), ogd, f"k={k} guidance stream (with pad)")
+    for out_f32 in (False, True):
+        g = torch.full((G,), -1.0, device=DEV)
+        y = _canary(n * (4 if out_f32 else 2), torch.float32 if out_f32 else torch.bfloat16)
+        c, sc = _canary(n // 2), _canary(n // 16)
+        st = torch.zeros(4, dtype=torch.int32, device=DEV)
+        tq.fakequant_rtn_onepass(X, G, g=g, out_dtype=tq.OUT_F32 if out_f32 else tq.OUT_BF16, out=y.view(X.shape),
+                                 codes_out=c, scales_out=sc, max_workgroups=cap, status=st)
+        torch.cuda.synchronize()
+        assert int(st[0]) == 0
+        oy, oc, os_ = oracle.fakequant_rtn(Xh, gX, None, G, out_f32)
+        assert_eq(g.cpu().numpy().view(np.uint32), gX.view(np.uint32), "rtn global scales")
+        if out_f32:
+            assert_f32_close(y.cpu().numpy(), oy, "rtn y f32")
+        else:
+            assert_eq(h16(y), oy, "rtn y bf16")
+        assert_eq(h8(c), oc, "rtn codes")
+        assert_eq(h8(sc), os_, "rtn scales")
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_onepass_bruteforce(tq, k):
     Yh = anchored_blocks()
