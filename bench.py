@@ -639,6 +639,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,
                      "kernel": f"k_fakequant_guided<{k},true,false> (trace_fakequant_guided, k={k}, bf16 out)",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
+        "elements_per_s": {"step": float(f"{n_total / (ms_step * 1e-3):.4g}"),
+                           "fakequant_guided": float(f"{n_total / (g_ms * 1e-3):.4g}")},
         "cpu_baseline": cpu,
         "mismatch": mism,
         "kernels": kernels,

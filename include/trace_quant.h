@@ -101,9 +101,10 @@ size_t trace_guidance_bytes(int64_t n, int k);
  * Enqueues three small kernels (clear, reduce, finalise). */
 int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_dev, void *stream);
 
-/* FP4 weight quantisation for the rollout's FP4 weight/activation GEMMs
- * ([en] opening paragraph and [ru] key facts: rollout runs with FP4 weights
- * and activations plus an FP4 KV cache).  Weights are not guided (rollout and
+/* FP4 weight quantisation for the rollout's FP4 weight/activation GEMMs (the
+ * opening paragraph of the page above, and the key facts of the Russian page
+ * "Alibaba Qwen представила TRACE: Rollout в FP4 ускоряется до 5,4 раза":
+ * rollout runs with FP4 weights and activations plus an FP4 KV cache).  Weights are not guided (rollout and
  * trainer hold the same weights), so no guidance stream is written.
  * w_bf16: bf16[n], G matrices of n / G contiguous elements each, blocks of 16
  * along the contiguous (GEMM reduction) dimension.  g_out: f32[G], written
