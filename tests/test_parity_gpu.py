@@ -370,6 +370,38 @@ def test_in_place_and_determinism(tq):
     assert torch.equal(codes, codes2) and torch.equal(gd, gd2) and torch.equal(scales, scales2)
 
 
+def test_in_place_every_fakequant(tq):
+    """Every fake-quant entry point with the output in the input's buffer
+    (bf16) gives the out-of-place result, codes included; the one-pass RTN in
+    one launch, with the excess read twice (one group larger than a capped
+    chip) and with one launch per group."""
+    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
+    g = tq.amax(Y)
+    codes, scales, gd2 = tq.quant_rollout(Y, g, 2)
+    gd4 = tq.guidance_pack(codes, scales, X.numel(), 4)
+    gx = tq.amax(X)
+    _, mxs, mxgd = tq.mx_quant_rollout(Y, 2)
+    cases = {
+        "guided": lambda x, o: tq.fakequant_guided(x, g, gd2, 2, out=o, codes_out=True),
+        "fullcode": lambda x, o: tq.fakequant_fullcode(x, g, gd4, out=o, codes_out=True),
+        "rtn shared": lambda x, o: tq.fakequant_rtn(x, g, scales, out=o, codes_out=True)[:2],
+        "rtn own": lambda x, o: tq.fakequant_rtn(x, gx, None, out=o, codes_out=True)[:2],
+        "mx guided": lambda x, o: tq.mx_fakequant_guided(x, mxgd, 2, out=o, codes_out=True),
+        "mx rtn own": lambda x, o: tq.mx_fakequant_rtn(x, None, out=o, codes_out=True)[:2],
+    }
+    for G, cap in ((1, 0), (1, 1), (4, 1)):            # one launch; excess read twice; one launch per 2 groups
+        cases[f"rtn one-pass G={G} cap={cap}"] = (
+            lambda x, o, G=G, cap=cap: tq.fakequant_rtn_onepass(x, G, out=o, codes_out=True, max_workgroups=cap)[1:3])
+    for name, fn in cases.items():
+        y_ref, c_ref = fn(X, None)
+        xin = X.clone()
+        y_in, c_in = fn(xin, xin)
+        torch.cuda.synchronize()
+        assert y_in.data_ptr() == xin.data_ptr(), name
+        assert torch.equal(xin.view(torch.int16), y_ref.view(torch.int16)), name
+        assert torch.equal(c_in, c_ref), name
+
+
 def test_guard_bytes_untouched(tq):
     """Outputs carved out of larger buffers filled with a canary: nothing
     outside the documented extents is written."""
@@ -486,23 +518,32 @@ def test_qat_autograd_wrappers(tq):
     assert torch.isfinite(w.grad).all() and x.grad is not None and torch.isfinite(x.grad.float()).all()
 
 
-@pytest.mark.parametrize("wl", [3, 4])
+@pytest.mark.parametrize("wl", [3, 4, 5])
 def test_kv_one_buffer_two_groups(tq, wl):
     """K and V of a layer in one [2, T, H, D] buffer with one global scale per
-    tensor (G = 2), as the benchmark runs the KV workloads; windows straddle
-    the K/V boundary."""
-    (_, shape), _ = synth.tensor_specs(wl)
-    K, Ky = synth.make_pair(wl, 0, shape, DEV)
-    V, Vy = synth.make_pair(wl, 1, shape, DEV)
+    tensor (G = 2), as the benchmark runs the KV workloads, through both the
+    two-kernel path and the one-pass path the benchmark picks (one launch for
+    the 2 x 32768 x 8 x 128 layer; one per group for the larger ones, which
+    exceed the on-chip capacity); windows straddle the K/V boundary."""
+    specs = synth.tensor_specs(wl)
+    pk, pv = (1, 2) if wl == 5 else (0, 1)
+    shape = specs[pk][1]
+    K, Ky = synth.make_pair(wl, pk, shape, DEV)
+    V, Vy = synth.make_pair(wl, pv, shape, DEV)
     X, Y = torch.stack([K, V]), torch.stack([Ky, Vy])
     del K, Ky, V, Vy
     nblk = X.numel() // 16
     half = nblk // 2
     wins = blocks_of(nblk, [(0, 400), (half - 300, half + 300), (nblk - 400, nblk)])
-    for k in synth.WORKLOADS[wl].ks:
-        c = Checker(tq, X, Y, k, 2)
-        c.run_gpu(out_f32=False)
-        c.check(wins)
+    for onepass in (None, 0):
+        for k in synth.WORKLOADS[wl].ks:
+            c = Checker(tq, X, Y, k, 2, onepass=onepass)
+            c.run_gpu(out_f32=False)
+            c.check(wins)
+            del c
+    check_rtn_onepass(tq, X, 2, 0, False, wins)
+    del X, Y
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
