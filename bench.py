@@ -190,9 +190,9 @@ def variant_stats(tq, sets, bufs, ns, Gs, K, k_main):
 def weight_stats(tq, K):
     """FP4 weight quantisation (trace_quant_weight) on 64 x 1024 x 2048 bf16
     expert weights, one global scale per expert matrix: per-kernel burst
-    timing of its amax and its RTN quantiser (no guidance), and the whole
-    call.  Algorithmic bytes read the weights once: 2 + 0.5 + 1/16 B per
-    element."""
+    timing of its amax and its RTN quantiser (no guidance), the whole call,
+    and the one-pass rollout without guidance, which gives the same results.
+    Algorithmic bytes read the weights once: 2 + 0.5 + 1/16 B per element."""
     import torch
     from precision_numerics_block_amd import synth
 
@@ -203,10 +203,16 @@ def weight_stats(tq, K):
     g = torch.empty(E, dtype=torch.float32, device=dev)
     codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+    work = torch.zeros(max(tq.onepass_work_bytes(E), 256), dtype=torch.uint8, device=dev)
     runs = {"weight_amax": (2.0, lambda: tq.amax(W, E, out=g)),
             "weight_quant": (2.0 + 0.5 + 1 / 16,
                              lambda: tq.quant_rollout(W, g, 2, E, guidance=False, codes=codes, scales=scales)),
-            "quant_weight": (2.0 + 0.5 + 1 / 16, lambda: tq.quant_weight(W, E, g=g, codes=codes, scales=scales))}
+            "quant_weight": (2.0 + 0.5 + 1 / 16, lambda: tq.quant_weight(W, E, g=g, codes=codes, scales=scales)),
+            # the same results from one read of the weights: every matrix fits on chip, so the one-pass
+            # rollout without guidance runs one launch per block of matrices
+            "quant_weight_onepass": (2.0 + 0.5 + 1 / 16,
+                                     lambda: tq.quant_rollout_onepass(W, 2, E, g=g, guidance=False, codes=codes,
+                                                                      scales=scales, work=work))}
     out = {"workload": f"expert weights {'x'.join(map(str, synth.WEIGHT_SHAPE))} bf16, G={E} (one per matrix)"}
     for nm, (bpe, fn) in runs.items():
         for _ in range(2):

@@ -93,6 +93,53 @@ def test_weight_full_size_sampled(tq):
         eq(h8(scales[e * per // 16:(e + 1) * per // 16]), os_, f"scales of expert {e}")
 
 
+@pytest.mark.parametrize("shape,cap", [((64, 64, 256), 1), ((8, 128, 256), 0)])
+def test_weight_onepass_small(tq, shape, cap):
+    """Weights through the one-pass rollout without guidance: with a cap of
+    one workgroup (33 tiles on chip) the 64 two-tile matrices take four
+    launches of 16 matrices; uncapped, one launch.  Every byte against the
+    oracle; the outputs start as a canary."""
+    W = synth.make_weights(shape, DEV)
+    G, n = shape[0], W.numel()
+    g = torch.full((G,), -1.0, device=DEV)
+    codes = torch.full((n // 2,), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((n // 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    tq.quant_rollout_onepass(W, 2, G, g=g, guidance=False, codes=codes, scales=scales, max_workgroups=cap)
+    torch.cuda.synchronize()
+    og, st = oracle.amax(h16(W), G)
+    assert st == 0
+    oc, os_, _ = oracle.quant_rollout(h16(W), og, 2, G, guidance=False)
+    eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    eq(h8(codes), oc, "codes")
+    eq(h8(scales), os_, "scales")
+
+
+def test_weight_onepass_full_size(tq):
+    """64 x 1024 x 2048 expert weights, G = 64, through the one-pass rollout
+    without guidance, as the benchmark times it (two launches of 32 matrices
+    on one MI355X): g, codes and scales equal trace_quant_weight's bit for
+    bit, and the oracle's for experts 0, 31, 32 and 63."""
+    shape = synth.WEIGHT_SHAPE
+    W = synth.make_weights(shape, DEV)
+    E, n = shape[0], W.numel()
+    g0, c0, s0 = tq.quant_weight(W, E)
+    g = torch.full((E,), -1.0, device=DEV)
+    codes = torch.full((n // 2,), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((n // 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    tq.quant_rollout_onepass(W, 2, E, g=g, guidance=False, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    assert torch.equal(g.view(torch.int32), g0.view(torch.int32))
+    assert torch.equal(codes, c0) and torch.equal(scales, s0)
+    og, st = oracle.amax(h16(W), E)
+    assert st == 0
+    eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    per = n // E
+    for e in (0, 31, 32, 63):
+        oc, os_, _ = oracle.quant_rollout(h16(W[e]), og[e:e + 1].copy(), 2, 1, guidance=False)
+        eq(h8(codes[e * per // 2:(e + 1) * per // 2]), oc, f"codes of expert {e}")
+        eq(h8(scales[e * per // 16:(e + 1) * per // 16]), os_, f"scales of expert {e}")
+
+
 def test_weight_writes_only_its_outputs(tq):
     """Outputs inside larger buffers: the guard bytes around codes and
     scales keep their sentinel (nothing like a guidance stream is written)."""
