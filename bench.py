@@ -323,16 +323,14 @@ def mismatch_stats(tq, pairs, bufs, k, Gs):
 def transport_stats(tq, graphs, sets, bufs, ns, Gs, K, k):
     """Guidance transport ("TRACE Core Concept": the guidance travels GPU ->
     CPU memory -> disk -> CPU -> GPU): per-stage rates for the compact (k)
-    and the full-code stream of the first tensor, and the step time when the
-    previous step's stream is copied to pinned host memory on a side stream
-    while the step runs."""
+    and the full-code stream of the first tensor, and the step time when
+    each step's stream is copied to pinned host memory after the step."""
     import tempfile
 
     import torch
 
     out = {}
     n, G = ns[0], Gs[0]
-    main = torch.cuda.current_stream()
     for label, kk, key in ((f"compact_k{k}", k, "gd"), ("full_k4", 4, "gd4")):
         b = bufs[0][0]
         rec = torch.empty(tq.record_bytes(n, kk, G), dtype=torch.uint8, pin_memory=True)
@@ -381,28 +379,24 @@ def transport_stats(tq, graphs, sets, bufs, ns, Gs, K, k):
 
     if not graphs:
         return out
-    side = torch.cuda.Stream()
 
+    # Each step's stream is copied right after the step on the same stream.
+    # On this runtime a device-to-host copy into pinned memory runs as a blit
+    # kernel on the compute units, and the one-pass kernels need every compute
+    # unit at once, so a copy on a side stream cannot overlap the step; it
+    # only delays a one-pass launch.  The serial form gives the cost per step.
     def run(key, kk):
         recs = [torch.empty(tq.record_bytes(n, kk, G), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-        done_step = [torch.cuda.Event() for _ in range(2 * K)]
-        done_copy = [torch.cuda.Event() for _ in range(2 * K)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(2 * K):                          # first K steps warm the pinned pages
             if i == K:
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
-            if key and i >= 2:
-                main.wait_event(done_copy[i - 2])      # set i % 2 is rewritten only after its copy
             graphs[i % 2].replay()
-            done_step[i].record(main)
             if key:
-                with torch.cuda.stream(side):
-                    side.wait_event(done_step[i])
-                    b = bufs[i % 2][0]
-                    tq.record_to_host(b[key], b["g"], n, kk, G, out=recs[i % 2])
-                    done_copy[i].record(side)
+                b = bufs[i % 2][0]
+                tq.record_to_host(b[key], b["g"], n, kk, G, out=recs[i % 2])
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / K
 
