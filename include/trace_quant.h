@@ -160,6 +160,11 @@ int64_t trace_onepass_capacity(int max_workgroups);
  * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s; the
  * environment variable TRACE_ONEPASS_WAIT_US, read at each call, replaces it,
  * which lets a test force the failure path); the outputs are then undefined.
+ * A launch needs one workgroup resident on every compute unit it uses at
+ * once: work on other streams that holds compute units (a device-to-host copy
+ * into pinned memory is such work, a blit kernel, on this runtime) delays it
+ * until that work ends, and two one-pass launches running at the same time
+ * on different streams can starve each other until the time limit.
  * Enqueues one kernel, or one per block of groups when the tensor exceeds
  * trace_onepass_capacity and its groups fit (see there); every launch writes
  * its groups' parts of the same output planes and leaves the work buffer
