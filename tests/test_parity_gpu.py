@@ -216,6 +216,23 @@ def test_workload_full_size_sampled(tq, wl, ti, G):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("k", [1, 3, 4])
+def test_full_size_other_widths(tq, k):
+    """The activations 64 x 512 x 2048 at the guidance widths the benchmark
+    also times (k = 1, 3) and the full code, in its launch configuration:
+    windows of blocks against the oracle."""
+    name, shape = synth.tensor_specs(2)[0]
+    X, Y = synth.make_pair(2, 0, shape, DEV)
+    nblk = X.numel() // 16
+    rng = np.random.default_rng(200 + k)
+    wins = [(0, 600), (nblk - 600, nblk)] + [(int(s), int(s) + 300) for s in rng.integers(0, nblk - 300, 6)]
+    c = Checker(tq, X, Y, k, 1)
+    c.run_gpu(out_f32=False)
+    c.check(blocks_of(nblk, wins))
+    del c, X, Y
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Brute force over every finite bf16 value
 # ---------------------------------------------------------------------------
