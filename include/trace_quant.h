@@ -98,7 +98,9 @@ size_t trace_guidance_bytes(int64_t n, int k);
  * x_bf16: bf16[n].  g_out: f32[G], written with amax(|x| over group) / 2688.
  * status_dev: nullable int*; if given and some input is inf or NaN,
  * TRACE_E_NONFINITE is stored there (never cleared: the caller zeroes it).
- * Enqueues three small kernels (clear, reduce, finalise). */
+ * Enqueues two kernels: a clear of g_out, then the reduction, in which each
+ * workgroup raises its group's g with an atomic max of fl(its amax / 2688)
+ * (the division rounds monotonically, so the largest is fl(amax / 2688)). */
 int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_dev, void *stream);
 
 /* FP4 weight quantisation for the rollout's FP4 weight/activation GEMMs (the

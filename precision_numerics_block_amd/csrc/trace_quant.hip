@@ -640,7 +640,12 @@ __global__ void k_amax_clear(uint32_t *g_bits, int G)
 // kPerformed: use the returning form of the atomic and wait for it, so the
 // maximum has been performed at the device's coherence point when the
 // function returns (the one-pass kernel's barrier arrival depends on it).
-template <int T = kAmaxThreads, bool kPerformed = false>
+// kScale: publish the global scale fl(A / 2688) of the workgroup's maximum A
+// instead of A.  x -> fl(x / 2688) is monotonic (IEEE division rounds
+// correctly), so the largest published scale is fl(max A / 2688): the group's
+// global scale, with no pass after the reduction.  Non-negative floats order
+// like their bit patterns, so the integer atomic max serves both forms.
+template <int T = kAmaxThreads, bool kPerformed = false, bool kScale = false>
 __device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint32_t *word)
 {
     uint32_t m = run;
@@ -654,6 +659,8 @@ __device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint3
         for (int i = 0; i < T / 64; ++i)
             b = max(b, wmax[i]);
         b <<= 16;
+        if (kScale)
+            b = as_u(as_f(b) / 2688.0f);
         if (b > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
             if (kPerformed) {
                 wmax[0] = __hip_atomic_fetch_max(word, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -666,7 +673,8 @@ __device__ __forceinline__ void amax_publish(uint32_t run, uint32_t *wmax, uint3
     __syncthreads();
 }
 
-// Group amax as float bits (|bf16| << 16 orders like the float).  Work items
+// Global scale per group, g = fl(amax / 2688), raised by each workgroup with
+// an atomic max on the float bits (amax_publish, kScale).  Work items
 // are (group, tile) pairs, walked grid-stride (neighbouring workgroups read
 // neighbouring tiles at each step) or, with `runs`, as one contiguous run per
 // workgroup.  Each thread keeps a running max for the current group and the
@@ -691,7 +699,7 @@ __global__ void __launch_bounds__(kAmaxThreads)
         uint32_t tile = w - grp * tiles_per_group;
         if (grp != cur) {
             if (cur != 0xffffffffu) {
-                amax_publish(run, wmax, g_bits + cur);
+                amax_publish<kAmaxThreads, false, true>(run, wmax, g_bits + cur);
                 run = 0;
             }
             cur = grp;
@@ -710,14 +718,7 @@ __global__ void __launch_bounds__(kAmaxThreads)
                 run = max(run, chunk_amax_finite(b[u], status));
     }
     if (cur != 0xffffffffu)
-        amax_publish(run, wmax, g_bits + cur);
-}
-
-__global__ void k_amax_finalize(float *g, int G)
-{
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < G)
-        g[i] = g[i] / 2688.0f;                   // g[i] holds the amax bits
+        amax_publish<kAmaxThreads, false, true>(run, wmax, g_bits + cur);
 }
 
 // RTN codes, scale bytes and (with gd_scales) guidance bits of one lane's U
@@ -2169,7 +2170,6 @@ int trace_amax(const void *x_bf16, int64_t n, int G, float *g_out, int *status_d
     hipLaunchKernelGGL(k_amax_clear, dim3((G + 255) / 256), dim3(256), 0, st, (uint32_t *)g_out, G);
     hipLaunchKernelGGL(k_amax, dim3(grid), dim3(kAmaxThreads), 0, st, (const u32x4 *)x_bf16, cpg, tpg,
                        (uint32_t)items, (uint32_t *)g_out, status_dev, runs);
-    hipLaunchKernelGGL(k_amax_finalize, dim3((G + 255) / 256), dim3(256), 0, st, g_out, G);
     return launched();
 }
 
