@@ -14,7 +14,7 @@ import torch
 
 from . import trace_quant as tq
 
-__all__ = ["guided_fake_quant", "fullcode_fake_quant", "rtn_fake_quant"]
+__all__ = ["guided_fake_quant", "fullcode_fake_quant", "rtn_fake_quant", "own_scale_fake_quant"]
 
 
 class _GuidedFakeQuant(torch.autograd.Function):
@@ -50,6 +50,17 @@ class _RtnFakeQuant(torch.autograd.Function):
         return gy, None, None, None
 
 
+class _OwnScaleFakeQuant(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, G, work):
+        _, y, _, _ = tq.fakequant_rtn_onepass(x.contiguous(), G, work=work)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        return gy, None, None
+
+
 def guided_fake_quant(x, g, guidance, k=2, G=1):
     """Rollout-guided FP4 fake-quant of bf16 `x` (GPU) with the rollout's
     global scales `g` and k-bit guidance stream; straight-through gradient."""
@@ -62,6 +73,16 @@ def fullcode_fake_quant(x, g, guidance, G=1):
 
 
 def rtn_fake_quant(x, g, scales=None, G=1):
-    """Plain RTN fake-quant (own block scales when `scales` is None, then `g`
-    should be the amax of x); straight-through gradient."""
+    """Plain RTN fake-quant (own block scales when `scales` is None; then `g`
+    should be x's own global scales, from trace_amax on x); straight-through
+    gradient."""
     return _RtnFakeQuant.apply(x, g, scales, G)
+
+
+def own_scale_fake_quant(x, G=1, work=None):
+    """Plain QAT fake-quant with the tensor's own scales (its global scale per
+    group and its block scales, as the rollout would compute them), from one
+    read of x where a group fits on chip; straight-through gradient.  `work`:
+    the one-pass work buffer (uint8, onepass_work_bytes(G) bytes, zero-filled
+    before its first use and left zeroed by every call); None allocates one."""
+    return _OwnScaleFakeQuant.apply(x, G, work)

@@ -519,6 +519,8 @@ def test_qat_autograd_wrappers(tq):
         (lambda x: qat.fullcode_fake_quant(x, g, gd4), lambda: tq.fakequant_fullcode(X, g, gd4)[0]),
         (lambda x: qat.rtn_fake_quant(x, gx), lambda: tq.fakequant_rtn(X, gx)[0]),
         (lambda x: qat.rtn_fake_quant(x, g, scales), lambda: tq.fakequant_rtn(X, g, scales)[0]),
+        (lambda x: qat.own_scale_fake_quant(x), lambda: tq.fakequant_rtn(X, gx)[0]),
+        (lambda x: qat.own_scale_fake_quant(x, 4), lambda: tq.fakequant_rtn(X, tq.amax(X, 4), None, 4)[0]),
     ]
     for fwd, ref in cases:
         x = X.clone().requires_grad_(True)
