@@ -629,6 +629,22 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # Same-run reference: torch's device copy of a 256 MiB buffer (the
+    # runtime's blit kernel), 2 bytes moved per byte copied.
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    for i in range(3):
+        dsts[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(20):
+        dsts[i % 2].copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() / (a.elapsed_time(e) / 20 * 1e-3) / 1e9
+    del src, dsts
+
     bad = [int(b["st"][0].item()) for bs in bufs for b in bs if int(b["st"][0].item()) != 0]
     if bad:                                      # e.g. a one-pass launch whose workgroups were not all resident
         raise RuntimeError(f"device status words report {bad} ({tq.lib.trace_status_str(bad[0]).decode()})")
@@ -676,6 +692,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,
                      "kernel": f"k_fakequant_guided<{k},true,false> (trace_fakequant_guided, k={k}, bf16 out)",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
+        "copy_reference": {"GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                           "what": "torch copy_ of a 256 MiB buffer on the same GPU in the same run (runtime blit "
+                                   "kernel), read + write bytes"},
         "elements_per_s": {"step": float(f"{n_total / (ms_step * 1e-3):.4g}"),
                            "fakequant_guided": float(f"{n_total / (g_ms * 1e-3):.4g}")},
         "cpu_baseline": cpu,
