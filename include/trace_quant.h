@@ -51,7 +51,7 @@
  *   - argument errors are found before anything is enqueued and returned as
  *     a negative trace_status (nothing is written); TRACE_E_HIP reports a
  *     failed launch; inputs must be finite (trace_amax can flag violations);
- *   - n > 0, n % 16 == 0, n % (16 * G) == 0, n < 2^35, 1 <= G <= n / 16;
+ *   - n > 0, n % 16 == 0, n % (16 * G) == 0, n < 2^34, 1 <= G <= n / 16;
  *   - every pointer 16-byte aligned; x / y_out may be the same buffer
  *     (in-place fake-quant); any other overlap is undefined.
  */
@@ -233,7 +233,7 @@ int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, co
  * val * X (exact).  The pages use the two-level NVFP4-style scale above; the
  * guided rule of "TRACE Core Concept" is the same on MX-normalised values.
  * Guidance stream: [ scale plane: n/32 E8M0 bytes | zero pad to a multiple of
- * 256 | bits ], bits as above.  Sizes: n > 0, n % 32 == 0, n < 2^35; 16-byte
+ * 256 | bits ], bits as above.  Sizes: n > 0, n % 32 == 0, n < 2^34; 16-byte
  * aligned pointers; scale bytes 0 .. 254 (255, E8M0's NaN, is not accepted
  * as input). */
 

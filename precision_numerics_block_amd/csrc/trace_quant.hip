@@ -588,7 +588,7 @@ __device__ __forceinline__ void store_bits(uint8_t *gd_bits, uint32_t c, uint32_
         // 3 bytes at 3c: a 2-byte store on the even-aligned side and a 1-byte
         // store on the other (offsets chosen per lane, no divergent branch)
         uint32_t b = compact_k3(cw), odd = c & 1u;
-        uint32_t o16 = 3 * c + odd, o8 = 3 * c + (odd ? 0u : 2u);
+        size_t o16 = 3 * (size_t)c + odd, o8 = 3 * (size_t)c + (odd ? 0u : 2u);   // 3c passes 2^32
         *reinterpret_cast<uint16_t *>(gd_bits + o16) = (uint16_t)(odd ? b >> 8 : b);
         gd_bits[o8] = (uint8_t)(odd ? b : b >> 16);
     } else if (K == 2) {
@@ -602,8 +602,9 @@ __device__ __forceinline__ void store_bits(uint8_t *gd_bits, uint32_t c, uint32_
 __device__ __forceinline__ uint32_t load_bits3(const uint8_t *gd_bits, uint32_t c)
 {
     uint32_t odd = c & 1u;
-    uint32_t h = *reinterpret_cast<const uint16_t *>(gd_bits + 3 * c + odd);
-    uint32_t b = gd_bits[3 * c + (odd ? 0u : 2u)];
+    size_t o = 3 * (size_t)c;                     // passes 2^32 for large tensors
+    uint32_t h = *reinterpret_cast<const uint16_t *>(gd_bits + o + odd);
+    uint32_t b = gd_bits[o + (odd ? 0u : 2u)];
     return odd ? (b | (h << 8)) : (h | (b << 16));
 }
 
@@ -1741,7 +1742,9 @@ __global__ void __launch_bounds__(kThreads)
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-constexpr int64_t kMaxN = int64_t(1) << 35;   // chunk indices (n / 8) fit in 32 bits
+// Chunk counts (n / 8) stay below 2^31, so every 32-bit chunk index, tile
+// count and rounded-up sum in the kernels and their launch plans fits.
+constexpr int64_t kMaxN = int64_t(1) << 34;
 
 DivMagic make_div_magic(uint32_t d)
 {

@@ -70,6 +70,7 @@ def test_argument_errors_before_any_hip_call(tq):
     assert L.trace_amax(A, n, 0, A, None, None) == E_SIZE
     assert L.trace_amax(A, 1 << 36, 1, A, None, None) == E_SIZE
     assert L.trace_amax(A, 1 << 35, 1, A, None, None) == E_SIZE
+    assert L.trace_amax(A, 1 << 34, 1, A, None, None) == E_SIZE         # chunk counts stay below 2^31
     # null pointers
     assert L.trace_amax(None, n, 1, A, None, None) == E_NULL
     assert L.trace_quant_rollout(A, n, 1, None, 2, A, A, None, None) == E_NULL
