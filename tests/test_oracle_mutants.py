@@ -9,8 +9,9 @@ An unmodified copy taken through the same route must pass them.
 
 Mutants that cannot change any result are left out on purpose: e.g. dropping
 the saturation shortcut of the E4M3 encoder or of RTN (the literal nearest
-search saturates by itself), or storing the whole nibble for k < 4 (its low k
-bits are those of the magnitude index).
+search saturates by itself), storing the whole nibble for k < 4 (its low k
+bits are those of the magnitude index), or moving the MX clamp at the top of
+E8M0's range (the largest finite float gives code 252, so it is never hit).
 """
 import os
 import subprocess
@@ -22,7 +23,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "trace_oracle.c")
 
-# name -> (original text, planted text, occurrences)
+# name -> (original text, planted text, occurrences), or a list of such
+# substitutions planted together
 MUTANTS = {
     # global scale: amax / 448 instead of amax / (6 * 448)
     "global_scale_drops_6": ("g_out[gi] = A / 2688.0f;", "g_out[gi] = A / 448.0f;", 1),
@@ -70,6 +72,29 @@ MUTANTS = {
     "mx_wrong_emax": ("int shared = (e - 1) - 2;", "int shared = (e - 1) - 1;", 1),
     # MX dequantisation drops the sign
     "mx_dequant_drops_sign": ("return (nib & 8) ? -(float)y : (float)y;", "return (float)y;", 1),
+    # no clamp of the MX shared exponent at the bottom of E8M0's range (block maxima below 2^-125)
+    "mx_no_low_clamp": ("if (code < 0) code = 0;", "", 1),
+    # an all-zero MX block gets scale 1 (code 127) instead of code 0
+    "mx_zero_block_code": ("    if (!(amax > 0.0f))\n        return 0;", "    if (!(amax > 0.0f))\n        return 127;", 1),
+    # the full-code rule compares with the rollout value's magnitude, ignoring its sign
+    "fullcode_ignores_sign": ("pick_nearer(lo, hi, oracle_e2m1_value(r), v)",
+                              "pick_nearer(lo, hi, fabs(oracle_e2m1_value(r)), v)", 1),
+    # E4M3 subnormal scales flushed to zero
+    "e4m3_subnormals_flushed": ("return ldexp((double)m, -9);", "return 0.0 * m;", 1),
+    # dequantised values lose the code's sign
+    "dequant_drops_sign": ("return (nib & 8) ? -y : y;", "return y;", 1),
+    # the chosen code's sign taken from the chosen value (loses -0) instead of v
+    "guided_sign_from_chosen": ("return (signbit(v) ? 8 : 0) | magnitude_index_of(chosen);",
+                                "return (signbit(chosen) ? 8 : 0) | magnitude_index_of(chosen);", 2),
+    # the global amax misses each group's last element
+    "amax_skips_group_end": ("i < (gi + 1) * per; ++i", "i < (gi + 1) * per - 1; ++i", 1),
+    # no zero pad between the guidance scale plane and the bit plane
+    "no_guidance_pad": ("    int64_t sp = n / 16;\n    return (sp + 255) / 256 * 256;",
+                        "    int64_t sp = n / 16;\n    return sp;", 1),
+    # a k-bit field written and read most significant bit first (a consistent layout mistake)
+    "kbit_fields_reversed": [("if ((value >> j) & 1)", "if ((value >> (k - 1 - j)) & 1)", 1),
+                             ("value |= ((plane[p / 8] >> (p % 8)) & 1) << j;",
+                              "value |= ((plane[p / 8] >> (p % 8)) & 1) << (k - 1 - j);", 1)],
 }
 
 
@@ -79,9 +104,10 @@ CONTROL = "unmodified"
 def _build(name, tmp):
     src = open(SRC).read()
     if name != CONTROL:
-        orig, planted, count = MUTANTS[name]
-        assert src.count(orig) == count, f"{name}: expected {count} occurrence(s) of the original text"
-        src = src.replace(orig, planted)
+        subs = MUTANTS[name] if isinstance(MUTANTS[name], list) else [MUTANTS[name]]
+        for orig, planted, count in subs:
+            assert src.count(orig) == count, f"{name}: expected {count} occurrence(s) of {orig!r}"
+            src = src.replace(orig, planted)
     path = os.path.join(tmp, f"{name}.c")
     with open(path, "w") as f:
         f.write(src)

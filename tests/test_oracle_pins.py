@@ -405,6 +405,20 @@ def test_amax_nonfinite_and_groups(orc):
     X = bf16_bits(x)
     g, st_ = orc.amax(X, 2)
     assert st_ == 0 and g[0] == np.float32(1.0) / np.float32(2688.0) and g[1] == 1.0
+    # the maximum at every position of a group, the group's first and last
+    # included, and negative: g = |max| / 2688 for that group, the rest keep
+    # g = 1 / 2688 (closed form: 2688 / 2688 = 1 exactly)
+    for G in (1, 2, 4):
+        per = 64 // G
+        for grp in range(G):
+            for pos in (0, 1, per // 2, per - 2, per - 1):
+                for sign in (1.0, -1.0):
+                    y = np.ones(64, np.float32)
+                    y[grp * per + pos] = sign * 2688.0
+                    g, st_ = orc.amax(bf16_bits(y), G)
+                    want = np.full(G, np.float32(1.0) / np.float32(2688.0), np.float32)
+                    want[grp] = 1.0
+                    assert st_ == 0 and np.array_equal(g, want), (G, grp, pos, sign)
     Xb = X.copy()
     Xb[3] = 0x7F80                        # +inf
     assert orc.amax(Xb)[1] == -7
