@@ -91,6 +91,12 @@ MUTANTS = {
     # no zero pad between the guidance scale plane and the bit plane
     "no_guidance_pad": ("    int64_t sp = n / 16;\n    return (sp + 255) / 256 * 256;",
                         "    int64_t sp = n / 16;\n    return sp;", 1),
+    # +0 and -0 counted as two distinct candidates, so a nearest zero code reads as a tie (RTN fallback)
+    "zero_signs_distinct": ("if (val != best && nearer(best, val, (double)v) == 0) distinct = 2;",
+                            "if ((val != best || signbit(val) != signbit(best)) && nearer(best, val, (double)v) == 0)"
+                            " distinct = 2;", 1),
+    # an on-grid value no longer its own upper bracket end
+    "bracket_hi_excludes_grid": ("if (val >= x && val < H) H = val;", "if (val > x && val < H) H = val;", 1),
     # a k-bit field written and read most significant bit first (a consistent layout mistake)
     "kbit_fields_reversed": [("if ((value >> j) & 1)", "if ((value >> (k - 1 - j)) & 1)", 1),
                              ("value |= ((plane[p / 8] >> (p % 8)) & 1) << j;",
