@@ -31,6 +31,9 @@
  *   - the scale chain is IEEE fp32 with round-to-nearest-even and no fused
  *     operations: t = a_b / (6 g), s = E4M3(t), c = s * g, inv = 1 / c,
  *     v = y * inv (inv = 0 when c = 0, inv = FLT_MAX when 1/c overflows);
+ *     the pages fix no order of these operations, so this order (reciprocal,
+ *     then multiply, rather than y / c) is a convention: parity unpinned for
+ *     that choice alone (the pins fix everything around it);
  *   - E4M3 rounding is nearest with ties to the even code, saturating at
  *     448, subnormals kept;
  *   - RTN ties go to the even magnitude index (the even E2M1 mantissa);
