@@ -595,6 +595,8 @@ def main():
         ms_step, gpu_ms_step = run_steps(K, True)
     else:
         ms_step, gpu_ms_step = ms_eager, gpu_ms_eager
+    # spread: five more loops of K steps each, after the headline region
+    loops = sorted(run_steps(K, bool(graphs))[0] for _ in range(5))
 
     # timed region 2: per-kernel launch durations, K back-to-back launches of
     # each kernel on alternating input sets, HIP events on the launch stream
@@ -676,6 +678,7 @@ def main():
         "gpu_ms_per_step": round(gpu_ms_step, 4),
         "launch": "hip graph replay" if graphs else "eager",
         "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_5_loops": {"median": round(loops[2], 4), "min": round(loops[0], 4), "max": round(loops[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
