@@ -151,13 +151,15 @@ int64_t trace_onepass_capacity(int max_workgroups);
  * y_bf16: bf16[n]; g_out: f32[G], written; k, codes, scales, guidance: as
  * trace_quant_rollout.  work: device buffer of trace_onepass_work_bytes(G)
  * bytes, 16-byte aligned, owned by the caller, zero-filled before its first
- * use; every call leaves it zeroed again (the last workgroup to finish
- * clears it), so no fill is needed between calls and the call is one kernel
- * launch (graph-capturable); calls that share a work buffer must be ordered
- * on one stream; after a call that reports TRACE_E_BARRIER the buffer must
- * be zero-filled again.  max_workgroups: 0 = one per
+ * use; every call leaves it zeroed again, also one that reports
+ * TRACE_E_BARRIER (every workgroup counts out once, after its last use of the
+ * buffer, and the last one out clears it), so no fill is needed between calls
+ * and the call is one kernel launch (graph-capturable); calls that share a
+ * work buffer must be ordered on one stream.  max_workgroups: 0 = one per
  * compute unit; a smaller cap leaves compute units to concurrent work but
- * keeps less on chip.  status_dev: nullable int*, as trace_amax's
+ * keeps less on chip; TRACE_E_SIZE when the cap would give one workgroup a run
+ * of 2^30 or more chunks of 8 elements (the output spans are 32-bit).
+ * status_dev: nullable int*, as trace_amax's
  * (TRACE_E_NONFINITE), and TRACE_E_BARRIER if the workgroups were not all
  * resident within a time limit (1 s plus n * 2 bytes at 50 GB/s; the
  * environment variable TRACE_ONEPASS_WAIT_US, read at each call, replaces it,
@@ -222,6 +224,21 @@ int trace_fakequant_fullcode(const void *x_bf16, int64_t n, int G, const float *
  * scale RTN).  codes_out (u8[n/2]) and scales_out (u8[n/16]) are nullable. */
 int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales_in,
                         void *y_out, int out_dtype, uint8_t *codes_out, uint8_t *scales_out, void *stream);
+
+/* Backward pass of every fake-quant above for quantisation-aware training
+ * ("TRACE Core Concept": the training side fake-quantises; the pages fix no
+ * gradient): the straight-through estimator clipped at the quantiser's
+ * range.  gx = gy where |v| <= 6 and +0 where |v| > 6 (there the forward
+ * saturated at +-6, so its output does not move with x), v = x * inv with
+ * inv = 1 / (s * g) as in the forward (the scale chain of the conventions
+ * above; a NaN v counts as beyond the range).
+ * x_bf16: bf16[n], the forward's input; g: f32[G] and scales: u8[n/16], the
+ * scales the forward used (guided and full code: the rollout's g and the
+ * guidance stream's scale plane, i.e. its first n/16 bytes; shared-scale RTN:
+ * scales_in; own-scale RTN: its g and scales_out).  gy, gx: bf16[n] or
+ * f32[n] per grad_dtype (TRACE_OUT_BF16 / TRACE_OUT_F32); gx may be gy. */
+int trace_fakequant_ste_grad(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales,
+                             const void *gy, void *gx, int grad_dtype, void *stream);
 
 /* ---- MXFP4 variant -------------------------------------------------------
  * The block format of gfx950's scaled FP4 conversions (OCP Microscaling

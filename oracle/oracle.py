@@ -61,6 +61,7 @@ def lib():
             "oracle_fakequant_guided": (None, [vp, i64, i32, vp, vp, i32, i64, i64, vp, i32, vp]),
             "oracle_fakequant_fullcode": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp]),
             "oracle_fakequant_rtn": (None, [vp, i64, i32, vp, vp, i64, i64, vp, i32, vp, vp]),
+            "oracle_ste_mask": (None, [vp, i64, i32, vp, vp, i64, i64, vp]),
             "oracle_mx_scale": (u8, [f32]),
             "oracle_mx_scale_value": (f64, [u8]),
             "oracle_mx_bitplane_offset": (i64, [i64]),
@@ -215,6 +216,29 @@ def fakequant_rtn(x, g, scales_in=None, G=1, out_f32=False, b0=None, b1=None, co
     sout = np.zeros(n // 16, np.uint8)
     lib().oracle_fakequant_rtn(_p(x), n, G, _p(g), _p(sin), b0, b1, _p(y), int(out_f32), _p(c), _p(sout))
     return y, c, sout
+
+
+def ste_mask(x, g, scales, G=1, b0=None, b1=None):
+    """Clipped straight-through gradient mask u8[n]: 1 where |x * inv| <= 6
+    with the forward's scales (g f32[G], scales u8[n/16] or a guidance
+    stream, whose first n/16 bytes are the scale plane)."""
+    x = _u16(x).reshape(-1)
+    n = x.size
+    g = np.ascontiguousarray(g, np.float32)
+    sc = np.ascontiguousarray(np.asarray(scales, np.uint8).reshape(-1)[: n // 16])
+    b0, b1 = _range(n, b0, b1)
+    m = np.zeros(n, np.uint8)
+    lib().oracle_ste_mask(_p(x), n, G, _p(g), _p(sc), b0, b1, _p(m))
+    return m
+
+
+def ste_grad(x, g, scales, gy, G=1, b0=None, b1=None):
+    """The gradient itself: gy where the mask is 1, +0 elsewhere (gy as
+    float32 values or as uint16 bf16 bit patterns; the result has gy's
+    dtype)."""
+    m = ste_mask(x, g, scales, G, b0, b1)
+    gy = np.asarray(gy).reshape(-1)
+    return np.where(m.astype(bool), gy, np.zeros(1, gy.dtype))
 
 
 def unpack_nibbles(codes):

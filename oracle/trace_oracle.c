@@ -539,6 +539,29 @@ void oracle_fakequant_rtn(const uint16_t *x, int64_t n, int G, const float *g,
     }
 }
 
+/* Gradient mask of the fake-quant for quantisation-aware training, blocks
+ * [b0, b1).  The pages say the training side fake-quantises ([en] TRACE Core
+ * Concept) and nothing about its gradient.  Reading taken: the
+ * straight-through estimator clipped at the quantiser's range.  The forward
+ * rounds the normalised value v = x * inv (inv from the scales it used) to a
+ * signed E2M1 point; where |v| > 6, the largest E2M1 magnitude, it saturates
+ * at +-6, so its output stays put as x moves and the gradient there is zero;
+ * everywhere else the incoming gradient passes unchanged.  mask[e] = 1 where
+ * it passes.  A NaN v is not within the range. */
+void oracle_ste_mask(const uint16_t *x, int64_t n, int G, const float *g, const uint8_t *scales,
+                     int64_t b0, int64_t b1, uint8_t *mask)
+{
+    int64_t bpg = blocks_per_group(n, G);
+    for (int64_t b = b0; b < b1; ++b) {
+        float inv = inv_from_scale(scales[b], g[b / bpg]);
+        for (int i = 0; i < 16; ++i) {
+            int64_t e = 16 * b + i;
+            float v = oracle_bf16_to_f32(x[e]) * inv;
+            mask[e] = fabs((double)v) <= 6.0 ? 1 : 0;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* MXFP4 variant: 32-element blocks, E8M0 shared scale, no global scale */
 /* ------------------------------------------------------------------ */

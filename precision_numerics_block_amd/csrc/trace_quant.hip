@@ -1254,116 +1254,122 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     }
     __syncthreads();
     if (!passed) {
+        // Outputs are undefined.  This workgroup still counts out below, as
+        // every workgroup does (also one that arrives after the others gave
+        // up), so the last one out leaves the work buffer zeroed.
         if (threadIdx.x == 0 && a.status)
             *a.status = TRACE_E_BARRIER;
-        return;
-    }
-    // Global scales of the groups this workgroup touches, into LDS (groups
-    // past kOpGroupSlots, possible only for groups of a few tiles, are read
-    // per item by one lane of each wave).
-    const uint32_t g_first = kOneGroup ? 0u : i0 / a.tpg;
-    const uint32_t g_count = kOneGroup ? 1u : min((i0 + cnt - 1) / a.tpg - g_first + 1, (uint32_t)kOpGroupSlots);
-    for (uint32_t i = threadIdx.x; i < g_count; i += kOpThreads)
-        gslot[i] = as_f(group_amax_bits(a, g_first + i)) / 2688.0f;
-    __syncthreads();
-    // One group, rollout codes: its scale tables, from the global scale just read.
-    if constexpr (kTab) {
-        const uint32_t ns = min(g_count, kSlots);
-        for (uint32_t i = threadIdx.x; i < ns * 384u; i += kOpThreads) {
-            const uint32_t sl = i / 384u, e = i - sl * 384u;
-            const float gs = gslot[sl];
-            if (e < 256u)
-                stab[sl * 256u + e] = scale_table_entry(e, gs);
-            else
-                ctab[sl * 128u + e - 256u] = inv_combined(e4m3_decode(e - 256u), gs);
-        }
-        if (threadIdx.x < ns)
-            ktab[threadIdx.x] = scale_table_k(gslot[threadIdx.x]);
+    } else {
+        // Global scales of the groups this workgroup touches, into LDS (groups
+        // past kOpGroupSlots, possible only for groups of a few tiles, are read
+        // per item by one lane of each wave).
+        const uint32_t g_first = kOneGroup ? 0u : i0 / a.tpg;
+        const uint32_t g_count = kOneGroup ? 1u : min((i0 + cnt - 1) / a.tpg - g_first + 1, (uint32_t)kOpGroupSlots);
+        for (uint32_t i = threadIdx.x; i < g_count; i += kOpThreads)
+            gslot[i] = as_f(group_amax_bits(a, g_first + i)) / 2688.0f;
         __syncthreads();
-    }
-    // The tables of an item's group (slot = group - g_first, below kSlots by
-    // the host's choice; clamped so that a slip cannot leave the arrays).
-    auto tabs_for = [&](uint32_t grp) {
-        const uint32_t sl = kOneGroup ? 0u : min(grp - g_first, kSlots > 0 ? kSlots - 1 : 0u);
-        return GroupTabs{stab + sl * 256u, ctab + sl * 128u, kTab ? ktab[sl] : 0};
-    };
-
-    // ---- phase 2: quantise ------------------------------------------------
-    // Item positions are recomputed from a copy the compiler cannot see
-    // through, so the scalar values of phase 1 are not kept alive (in spilled
-    // SGPRs) across the barrier.
-    uint32_t p2_reg = i_reg, p2_lds = i_lds;
-    asm volatile("" : "+s"(p2_reg), "+s"(p2_lds));
-    if (blockIdx.x == 0) {
-        for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
-            a.g_out[i] = as_f(group_amax_bits(a, i)) / 2688.0f;
-        if (a.gd_scales)
-            zero_pad<kOpThreads>(a.gd_scales, a.pad_begin, a.pad_end);
-    }
-    auto gscale = [&](uint32_t grp) {
-        if (kOneGroup)
-            return gslot[0];
-        uint32_t i = grp - g_first;
-        if (i < (uint32_t)kOpGroupSlots)
-            return gslot[i];
-        uint32_t bits = 0;
-        if (__lane_id() == 0)
-            bits = group_amax_bits(a, grp);
-        return as_f(__builtin_amdgcn_readfirstlane(bits)) / 2688.0f;
-    };
-    // register tiles: straight-line code (tiles past nreg store nothing)
-    // the run of chunks this workgroup owns (items are consecutive, and with
-    // kSpan only the run's last item can be short)
-    const Item w_first = item_at<kOneGroup>(a, i0), w_last = item_at<kOneGroup>(a, i0 + cnt - 1);
-    const Outs span = outs_over<K, OUT>(a, w_first.first, w_last.first + w_last.count - w_first.first);
-    const Outs none = outs_over<K, OUT>(a, 0u, 0u);  // no records: every store dropped
-    auto outs_for = [&](const Item &w, bool live) {
-        // An item that is not live stores nothing wherever it lies (a batch of
-        // read-twice items can run past its last one into the LDS items).
-        if (!live)
-            return none;
-        return kSpan ? span : outs_over<K, OUT>(a, w.first, w.count);
-    };
-    // (gv: the item's global scale; with scale tables it is not needed, and
-    // not fetched, since the fetch past the LDS slots is a device-scope load)
-    auto block_out = [&](const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv) {
-        if constexpr (OUT == 0)
-            quant_block<K, kTab>(o, w, b, ab, gv, tabs_for(w.grp));
-        else
-            rtn_block<OUT>(o, w, b, ab, gv);
-    };
-    // (with span descriptors a register tile that is not live lies past the
-    // run's end, outside the records, so it needs no descriptor of its own)
-#pragma unroll
-    for (int h = 0; h < kOpRegTiles; ++h) {
-        Item w = item_at<kOneGroup>(a, p2_reg + h);
-        bool live = p2_reg + h < i0 + cnt;
-        block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live && !kTab ? gscale(w.grp) : 0.0f);
-    }
-    for (uint32_t j = 0; j < nlds; ++j) {
-        Item w = item_at<kOneGroup>(a, p2_lds + j);
-        Blk b = block_from_lds(lds_tiles, j);
-        block_out(outs_for(w, true), w, b, block_amax_bits(b), kTab ? 0.0f : gscale(w.grp));
-    }
-    for (uint32_t j = 0; j < nstr; j += kOpStream) {
-        Chunk x[kOpStream][2];
-        Item w[kOpStream];
-        for (int q = 0; q < kOpStream; ++q) {
-            w[q] = item_at<kOneGroup>(a, i0 + j + q);
-            load_item(a, w[q], j + q < nstr, x[q]);
+        // One group, rollout codes: its scale tables, from the global scale just read.
+        if constexpr (kTab) {
+            const uint32_t ns = min(g_count, kSlots);
+            for (uint32_t i = threadIdx.x; i < ns * 384u; i += kOpThreads) {
+                const uint32_t sl = i / 384u, e = i - sl * 384u;
+                const float gs = gslot[sl];
+                if (e < 256u)
+                    stab[sl * 256u + e] = scale_table_entry(e, gs);
+                else
+                    ctab[sl * 128u + e - 256u] = inv_combined(e4m3_decode(e - 256u), gs);
+            }
+            if (threadIdx.x < ns)
+                ktab[threadIdx.x] = scale_table_k(gslot[threadIdx.x]);
+            __syncthreads();
         }
-        for (int q = 0; q < kOpStream; ++q) {
-            bool live = j + q < nstr;
-            Blk b = to_block(x[q]);
-            block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live && !kTab ? gscale(w[q].grp) : 0.0f);
+        // The tables of an item's group (slot = group - g_first, below kSlots by
+        // the host's choice; clamped so that a slip cannot leave the arrays).
+        auto tabs_for = [&](uint32_t grp) {
+            const uint32_t sl = kOneGroup ? 0u : min(grp - g_first, kSlots > 0 ? kSlots - 1 : 0u);
+            return GroupTabs{stab + sl * 256u, ctab + sl * 128u, kTab ? ktab[sl] : 0};
+        };
+
+        // ---- phase 2: quantise ------------------------------------------------
+        // Item positions are recomputed from a copy the compiler cannot see
+        // through, so the scalar values of phase 1 are not kept alive (in spilled
+        // SGPRs) across the barrier.
+        uint32_t p2_reg = i_reg, p2_lds = i_lds;
+        asm volatile("" : "+s"(p2_reg), "+s"(p2_lds));
+        if (blockIdx.x == 0) {
+            for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
+                a.g_out[i] = as_f(group_amax_bits(a, i)) / 2688.0f;
+            if (a.gd_scales)
+                zero_pad<kOpThreads>(a.gd_scales, a.pad_begin, a.pad_end);
+        }
+        auto gscale = [&](uint32_t grp) {
+            if (kOneGroup)
+                return gslot[0];
+            uint32_t i = grp - g_first;
+            if (i < (uint32_t)kOpGroupSlots)
+                return gslot[i];
+            uint32_t bits = 0;
+            if (__lane_id() == 0)
+                bits = group_amax_bits(a, grp);
+            return as_f(__builtin_amdgcn_readfirstlane(bits)) / 2688.0f;
+        };
+        // register tiles: straight-line code (tiles past nreg store nothing)
+        // the run of chunks this workgroup owns (items are consecutive, and with
+        // kSpan only the run's last item can be short)
+        const Item w_first = item_at<kOneGroup>(a, i0), w_last = item_at<kOneGroup>(a, i0 + cnt - 1);
+        const Outs span = outs_over<K, OUT>(a, w_first.first, w_last.first + w_last.count - w_first.first);
+        const Outs none = outs_over<K, OUT>(a, 0u, 0u);  // no records: every store dropped
+        auto outs_for = [&](const Item &w, bool live) {
+            // An item that is not live stores nothing wherever it lies (a batch of
+            // read-twice items can run past its last one into the LDS items).
+            if (!live)
+                return none;
+            return kSpan ? span : outs_over<K, OUT>(a, w.first, w.count);
+        };
+        // (gv: the item's global scale; with scale tables it is not needed, and
+        // not fetched, since the fetch past the LDS slots is a device-scope load)
+        auto block_out = [&](const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv) {
+            if constexpr (OUT == 0)
+                quant_block<K, kTab>(o, w, b, ab, gv, tabs_for(w.grp));
+            else
+                rtn_block<OUT>(o, w, b, ab, gv);
+        };
+        // (with span descriptors a register tile that is not live lies past the
+        // run's end, outside the records, so it needs no descriptor of its own)
+    #pragma unroll
+        for (int h = 0; h < kOpRegTiles; ++h) {
+            Item w = item_at<kOneGroup>(a, p2_reg + h);
+            bool live = p2_reg + h < i0 + cnt;
+            block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live && !kTab ? gscale(w.grp) : 0.0f);
+        }
+        for (uint32_t j = 0; j < nlds; ++j) {
+            Item w = item_at<kOneGroup>(a, p2_lds + j);
+            Blk b = block_from_lds(lds_tiles, j);
+            block_out(outs_for(w, true), w, b, block_amax_bits(b), kTab ? 0.0f : gscale(w.grp));
+        }
+        for (uint32_t j = 0; j < nstr; j += kOpStream) {
+            Chunk x[kOpStream][2];
+            Item w[kOpStream];
+            for (int q = 0; q < kOpStream; ++q) {
+                w[q] = item_at<kOneGroup>(a, i0 + j + q);
+                load_item(a, w[q], j + q < nstr, x[q]);
+            }
+            for (int q = 0; q < kOpStream; ++q) {
+                bool live = j + q < nstr;
+                Blk b = to_block(x[q]);
+                block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live && !kTab ? gscale(w[q].grp) : 0.0f);
+            }
         }
     }
 
     // ---- departure: the last workgroup out leaves the work buffer zeroed ---
-    // Every workgroup read the group maxima (into gslot, before a barrier)
-    // and passed the arrival barrier before counting out, so nothing reads
-    // the words the last one clears; the next call on the stream starts after
-    // this kernel has finished.
+    // The barrier first: every wave of this workgroup has finished phase 2,
+    // including its reads of the group maxima (the per-item fallback past the
+    // LDS slots, and workgroup 0's g_out), before the workgroup counts out.
+    // Every workgroup counts out exactly once, after its last read of the
+    // work buffer, so nothing reads the words the last one clears; the next
+    // call on the stream starts after this kernel has finished.
+    __syncthreads();
     if (threadIdx.x == 0)
         tree_count(a.work + kOpDoneWord, P, &leaving_last);
     __syncthreads();
@@ -1560,6 +1566,71 @@ __global__ void __launch_bounds__(kThreads)
             store_y<TRACE_NT_STORE_RTN>(out, c, yv);
             if (kCodes)
                 st_stream<TRACE_NT_STORE_RTN>(cw, codes_out + c);
+        }
+    }
+}
+
+// Straight-through gradient of the fake-quant, clipped at the quantiser's
+// range: gx = gy where |v| <= 6 and 0 where |v| > 6 (the forward saturated
+// there, so its output does not move with x), v = x * inv with the inv =
+// 1 / (s * g) of the scales the forward used (pair_scales_from_bytes, as the
+// guided and shared-scale kernels compute it).  kF32: gradients in fp32,
+// else bf16.  gx may be gy.
+template <bool kOneGroup, bool kF32>
+__global__ void __launch_bounds__(kThreads)
+    k_ste_grad(const u32x4 *__restrict__ x, uint32_t nchunk, const float *__restrict__ g, DivMagic dm,
+               uint32_t last_group, const uint8_t *__restrict__ scales, const u32x4 *gy, u32x4 *gx)
+{
+    constexpr int W = kF32 ? 2 : 1;                     // 16-byte words of gradient per chunk
+    uint32_t ntiles = (nchunk + kTile - 1) / kTile;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        Chunk xc[kUnroll];
+        u32x4 gw[kUnroll][W];
+        uint32_t cs[kUnroll], sc[kUnroll];
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = t * kTile + u * kThreads + threadIdx.x;
+            cs[u] = c;
+            xc[u] = Chunk{{0u, 0u, 0u, 0u}};
+            sc[u] = 0u;
+            for (int h = 0; h < W; ++h)
+                gw[u][h] = u32x4{0u, 0u, 0u, 0u};
+            if (c < nchunk) {
+                xc[u] = load_chunk(x, c);
+                sc[u] = scales[c >> 1];
+                for (int h = 0; h < W; ++h)
+                    gw[u][h] = ld_stream(gy + (size_t)W * c + h);
+            }
+        }
+        if (cs[0] >= nchunk)
+            continue;
+        float gg[kUnroll];
+        for (int u = 0; u < kUnroll; ++u)
+            gg[u] = group_scale<kOneGroup>(g, cs[u] >> 1, dm, last_group);
+        PairScales ps = pair_scales_from_bytes(sc[0], sc[1], gg[0], gg[1]);
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t c = cs[u];
+            if (c >= nchunk)
+                continue;
+            uint32_t keep = 0;                          // bit i: element i passes its gradient
+            for (int i = 0; i < 8; ++i) {
+                uint32_t w = xc[u].w[i >> 1];
+                float v = ((i & 1) ? bf_hi(w) : bf_lo(w)) * ps.inv[u];
+                keep |= (fabsf(v) <= 6.0f ? 1u : 0u) << i;
+            }
+            for (int h = 0; h < W; ++h) {
+                u32x4 o = gw[u][h];
+                if constexpr (kF32) {                     // one element per word
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = ((keep >> (4 * h + j)) & 1u) ? o[j] : 0u;
+                } else {                                  // two bf16 per word, element 2m low
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t m = (((keep >> (2 * j)) & 1u) ? 0x0000ffffu : 0u) |
+                                     (((keep >> (2 * j + 1)) & 1u) ? 0xffff0000u : 0u);
+                        o[j] &= m;
+                    }
+                }
+                st_stream<TRACE_NT_STORE_RTN>(o, gx + (size_t)W * c + h);
+            }
         }
     }
 }
@@ -1913,10 +1984,31 @@ int64_t trace_onepass_capacity(int max_workgroups)
 
 namespace {
 
+// Output descriptors over a workgroup's run of chunks hold 32-bit byte
+// counts and offsets: the longest run (items spread over `grid` workgroups)
+// times the widest output plane's bytes per chunk (4 for rollout codes and
+// guidance bits, 16 / 32 for bf16 / f32 fake-quant outputs) must stay below
+// 2^32.  Only a small workgroup cap on a large tensor can exceed it.
+bool onepass_run_fits(uint64_t items, int64_t grid, uint32_t bytes_per_chunk)
+{
+    const uint64_t run = (items + (uint64_t)grid - 1) / (uint64_t)grid * (uint64_t)kOpTile;
+    return run * bytes_per_chunk < (uint64_t(1) << 32);
+}
+
+// The same test before any device query, for one group under an explicit
+// workgroup cap (the grid is at most the cap, so the run is at least this).
+bool onepass_cap_fits(int64_t n, int G, int max_workgroups, uint32_t bytes_per_chunk)
+{
+    if (G != 1 || max_workgroups <= 0)
+        return true;
+    const uint64_t items = ((uint64_t)n / 8 + kOpTile - 1) / kOpTile;
+    return onepass_run_fits(items, max_workgroups, bytes_per_chunk);
+}
+
 // The launch parameters shared by both one-pass entry points (arguments
 // already checked): the item layout, the barrier limit and the grid.
 int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work, int max_workgroups,
-                 int *status_dev, OnePass &a, int64_t &grid, size_t &lds)
+                 int *status_dev, uint32_t bytes_per_chunk, OnePass &a, int64_t &grid, size_t &lds)
 {
     OnePassDevice d;
     int rc = onepass_device(d);
@@ -1948,6 +2040,8 @@ int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work
         grid = max_workgroups;
     if (grid > (int64_t)a.items)
         grid = a.items;
+    if (!onepass_run_fits(a.items, grid, bytes_per_chunk))
+        return TRACE_E_SIZE;
     lds = (size_t)a.lds_tiles * kOpTile * 16;
     return TRACE_OK;
 }
@@ -1990,7 +2084,7 @@ int rollout_onepass_launch(const void *y_bf16, int64_t n, int G, int k, float *g
     OnePass a;
     int64_t grid;
     size_t lds;
-    int rc = onepass_plan(y_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds);
+    int rc = onepass_plan(y_bf16, n, G, g_out, work, max_workgroups, status_dev, 4u, a, grid, lds);
     if (rc != TRACE_OK)
         return rc;
     a.codes = (uint32_t *)codes;
@@ -2045,7 +2139,7 @@ int rtn_onepass_launch(const void *x_bf16, int64_t n, int G, float *g_out, void 
     OnePass a;
     int64_t grid;
     size_t lds;
-    int rc = onepass_plan(x_bf16, n, G, g_out, work, max_workgroups, status_dev, a, grid, lds);
+    int rc = onepass_plan(x_bf16, n, G, g_out, work, max_workgroups, status_dev, f32 ? 32u : 16u, a, grid, lds);
     if (rc != TRACE_OK)
         return rc;
     a.codes = (uint32_t *)codes_out;
@@ -2069,27 +2163,33 @@ int rtn_onepass_launch(const void *x_bf16, int64_t n, int G, float *g_out, void 
     return launched();
 }
 
-}  // namespace
-
-extern "C" {
-
-int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
-                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
-                                int *status_dev, void *stream)
+// Argument checks of the one-pass rollout entry points (with or without a
+// caller-owned work buffer), before anything touches the device.
+int rollout_onepass_check(const void *y_bf16, int64_t n, int G, int k, const float *g_out, const uint8_t *codes,
+                          const uint8_t *scales, const uint8_t *guidance, bool need_work, const void *work,
+                          int max_workgroups, const int *status_dev)
 {
     int rc = check_sizes(n, G);
     if (rc)
         return rc;
-    if (!y_bf16 || !g_out || !codes || !scales || !work)
+    if (!y_bf16 || !g_out || !codes || !scales || (need_work && !work))
         return TRACE_E_NULL;
     if (!aligned16(y_bf16) || !aligned16(g_out) || !aligned16(codes) || !aligned16(scales) ||
-        (guidance && !aligned16(guidance)) || !aligned16(work) || (status_dev && !aligned16(status_dev)))
+        (guidance && !aligned16(guidance)) || (need_work && !aligned16(work)) ||
+        (status_dev && !aligned16(status_dev)))
         return TRACE_E_ALIGN;
     if (k < 1 || k > 4)
         return TRACE_E_K;
-    if (max_workgroups < 0)
+    if (max_workgroups < 0 || !onepass_cap_fits(n, G, max_workgroups, 4u))
         return TRACE_E_SIZE;
-    int gpb;
+    return TRACE_OK;
+}
+
+// The one-pass rollout over checked arguments with the given work buffer.
+int rollout_onepass_run(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes, uint8_t *scales,
+                        uint8_t *guidance, void *work, int max_workgroups, int *status_dev, hipStream_t st)
+{
+    int gpb, rc;
     if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
         return rc;
     const int64_t per = n / G, bits = bitplane_offset(n);
@@ -2100,11 +2200,27 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
                                     codes + e0 / 2, scales + e0 / 16, guidance ? guidance + e0 / 16 : nullptr,
                                     guidance ? guidance + bits + e0 * k / 8 : nullptr,
                                     g0 == 0 ? (uint32_t)(n / 16) : 0u, g0 == 0 ? (uint32_t)bits : 0u, work,
-                                    max_workgroups, status_dev, (hipStream_t)stream);
+                                    max_workgroups, status_dev, st);
         if (rc != TRACE_OK)
             return rc;
     }
     return TRACE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
+                                int *status_dev, void *stream)
+{
+    int rc = rollout_onepass_check(y_bf16, n, G, k, g_out, codes, scales, guidance, true, work, max_workgroups,
+                                   status_dev);
+    if (rc != TRACE_OK)
+        return rc;
+    return rollout_onepass_run(y_bf16, n, G, k, g_out, codes, scales, guidance, work, max_workgroups, status_dev,
+                               (hipStream_t)stream);
 }
 
 int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, int out_dtype,
@@ -2121,7 +2237,7 @@ int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_o
         return TRACE_E_ALIGN;
     if (out_dtype != TRACE_OUT_BF16 && out_dtype != TRACE_OUT_F32)
         return TRACE_E_DTYPE;
-    if (max_workgroups < 0)
+    if (max_workgroups < 0 || !onepass_cap_fits(n, G, max_workgroups, out_dtype == TRACE_OUT_F32 ? 32u : 16u))
         return TRACE_E_SIZE;
     int gpb;
     if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
@@ -2319,6 +2435,34 @@ int trace_fakequant_rtn(const void *x_bf16, int64_t n, int G, const float *g, co
     return launch_rtn<true>(L, x_bf16, g, nullptr, out, codes_out, scales_out);
 }
 
+int trace_fakequant_ste_grad(const void *x_bf16, int64_t n, int G, const float *g, const uint8_t *scales,
+                             const void *gy, void *gx, int grad_dtype, void *stream)
+{
+    int rc = check_sizes(n, G);
+    if (rc)
+        return rc;
+    if (!x_bf16 || !g || !scales || !gy || !gx)
+        return TRACE_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(g) || !aligned16(scales) || !aligned16(gy) || !aligned16(gx))
+        return TRACE_E_ALIGN;
+    if (grad_dtype != TRACE_OUT_BF16 && grad_dtype != TRACE_OUT_F32)
+        return TRACE_E_DTYPE;
+    Launch L = plan(n, G, stream);
+    const u32x4 *xp = (const u32x4 *)x_bf16, *gyp = (const u32x4 *)gy;
+    u32x4 *gxp = (u32x4 *)gx;
+    (void)hipGetLastError();
+#define TRACE_S(ONE, F32)                                                                                         \
+    hipLaunchKernelGGL((k_ste_grad<ONE, F32>), L.grid, dim3(kThreads), 0, L.st, xp, L.nchunk, g, L.dm, L.last,   \
+                       scales, gyp, gxp)
+    if (L.one) {
+        if (grad_dtype == TRACE_OUT_F32) TRACE_S(true, true); else TRACE_S(true, false);
+    } else {
+        if (grad_dtype == TRACE_OUT_F32) TRACE_S(false, true); else TRACE_S(false, false);
+    }
+#undef TRACE_S
+    return launched();
+}
+
 // ---- MXFP4 variant --------------------------------------------------------
 static int mx_check_sizes(int64_t n)
 {
@@ -2441,7 +2585,7 @@ const char *trace_status_str(int status)
     switch (status) {
     case TRACE_OK: return "ok";
     case TRACE_E_NULL: return "a required pointer is NULL";
-    case TRACE_E_SIZE: return "n or G violates the size rules (n > 0, n % 16 == 0, n % (16 G) == 0, n < 2^35)";
+    case TRACE_E_SIZE: return "n or G violates the size rules (n > 0, n % 16 == 0, n % (16 G) == 0, n < 2^34)";
     case TRACE_E_ALIGN: return "a pointer is not 16-byte aligned";
     case TRACE_E_K: return "unsupported guidance width k";
     case TRACE_E_DTYPE: return "unknown output dtype";

@@ -36,6 +36,7 @@ _SIGS = {
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_rtn": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp]),
+    "trace_fakequant_ste_grad": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp, _int, _vp]),
     "trace_mx_scale_bytes": (_sz, [_i64]),
     "trace_mx_guidance_bytes": (_sz, [_i64, _int]),
     "trace_mx_quant_rollout": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp]),
@@ -62,7 +63,7 @@ OUT_BF16, OUT_F32 = 0, 1
 __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout", "quant_weight",
     "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass", "fakequant_rtn_onepass",
-    "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "version",
+    "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "fakequant_ste_grad", "version",
     "mx_scale_bytes", "mx_guidance_bytes", "mx_quant_rollout", "mx_fakequant_guided", "mx_fakequant_rtn",
     "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
     "record_read", "xxh64",
@@ -268,6 +269,28 @@ def fakequant_rtn(x, g, scales_in=None, G=1, out_dtype=OUT_BF16, out=None, codes
         _ptr(x), x.numel(), int(G), _ptr(g), _ptr(scales_in), _ptr(out), int(out_dtype),
         _ptr(codes_out), _ptr(scales_out), _stream(x.device)))
     return out, codes_out, scales_out
+
+
+def fakequant_ste_grad(x, g, scales, gy, G=1, out=None):
+    """Clipped straight-through gradient: gy where |x * inv| <= 6, else 0,
+    with the forward's scales (g f32[G], scales u8[n/16]; a guidance stream
+    may be passed as ``scales``: its first n/16 bytes are the scale plane).
+    gy is bf16 or f32 with x's shape; ``out`` may be gy (in place)."""
+    _need(x, torch.bfloat16, "x")
+    _need(g, torch.float32, "g")
+    _need(scales, torch.uint8, "scales")
+    if not isinstance(gy, torch.Tensor) or gy.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("gy must be a bf16 or f32 GPU tensor")
+    _need(gy, gy.dtype, "gy")
+    if gy.numel() != x.numel():
+        raise ValueError("gy must have x's number of elements")
+    if scales.numel() < x.numel() // 16:
+        raise ValueError("scales must hold n / 16 bytes")
+    out = torch.empty_like(gy) if out is None else _need(out, gy.dtype, "out")
+    _check("trace_fakequant_ste_grad", lib.trace_fakequant_ste_grad(
+        _ptr(x), x.numel(), int(G), _ptr(g), _ptr(scales), _ptr(gy), _ptr(out),
+        OUT_F32 if gy.dtype == torch.float32 else OUT_BF16, _stream(x.device)))
+    return out
 
 
 # ---- MXFP4 variant (32-element blocks, E8M0 scales, no global scale) ------

@@ -55,6 +55,7 @@ def test_sizes(tq):
     assert tq.onepass_work_bytes(1) == 8960 and tq.onepass_work_bytes(64) == 8960
     assert tq.onepass_work_bytes(65) == 9216 and tq.onepass_work_bytes(0) == 0
     assert "barrier" in tq.lib.trace_status_str(-10).decode()
+    assert "2^34" in tq.lib.trace_status_str(-2).decode()
     assert tq.mx_scale_bytes(32 * 10) == 10 and tq.mx_scale_bytes(16) == 0
     assert tq.mx_guidance_bytes(32 * 10, 2) == 256 + 80 and tq.mx_guidance_bytes(32 * 10, 5) == 0
     assert tq.onepass_capacity(-1) == 0                 # argument error, before any device query
@@ -120,6 +121,10 @@ def test_argument_errors_before_any_hip_call(tq):
     assert rop(A, n, 1, A, A, 0, A + 8, None, A, 0, None, None) == E_ALIGN
     assert rop(A, n, 1, A, A, 5, None, None, A, 0, None, None) == E_DTYPE
     assert rop(A, n, 1, A, A, 0, None, None, A, -2, None, None) == E_SIZE
+    # a workgroup cap that would give one workgroup a run of 2^30 chunks or
+    # more (32-bit output spans): rejected before the device query
+    assert op(A, 1 << 33, 1, 4, A, A, A, A, A, 1, None, None) == E_SIZE        # codes: 2^30 chunks x 4 B
+    assert rop(A, 1 << 30, 1, A, A, 1, None, None, A, 1, None, None) == E_SIZE  # f32 y: 2^27 chunks x 32 B
     # MX variant
     assert L.trace_mx_quant_rollout(A, 48, 2, A, A, None, None) == E_SIZE
     assert L.trace_mx_quant_rollout(A, n, 2, None, A, None, None) == E_NULL

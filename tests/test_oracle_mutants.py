@@ -101,6 +101,16 @@ MUTANTS = {
     "kbit_fields_reversed": [("if ((value >> j) & 1)", "if ((value >> (k - 1 - j)) & 1)", 1),
                              ("value |= ((plane[p / 8] >> (p % 8)) & 1) << j;",
                               "value |= ((plane[p / 8] >> (p % 8)) & 1) << (k - 1 - j);", 1)],
+    # the gradient mask: the saturation edge itself excluded (|v| < 6 instead of <= 6)
+    "ste_strict_edge": ("mask[e] = fabs((double)v) <= 6.0 ? 1 : 0;", "mask[e] = fabs((double)v) < 6.0 ? 1 : 0;", 1),
+    # the gradient mask compares the raw input with 6, forgetting the scales
+    "ste_ignores_scales": ("mask[e] = fabs((double)v) <= 6.0 ? 1 : 0;",
+                           "mask[e] = fabs((double)oracle_bf16_to_f32(x[e])) <= 6.0 ? 1 : 0;", 1),
+    # the gradient mask inverted (passes only where the forward saturated)
+    "ste_mask_inverted": ("mask[e] = fabs((double)v) <= 6.0 ? 1 : 0;", "mask[e] = fabs((double)v) <= 6.0 ? 0 : 1;", 1),
+    # each block takes the first group's global scale
+    "ste_first_group_only": ("float inv = inv_from_scale(scales[b], g[b / bpg]);",
+                             "float inv = inv_from_scale(scales[b], g[0]);", 1),
 }
 
 

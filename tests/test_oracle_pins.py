@@ -599,3 +599,96 @@ def test_mx_worked_example_and_rules(orc):
     _, sc, _ = orc.mx_quant_rollout(Y, 2)
     np.testing.assert_array_equal(so, sc)
 
+
+
+# --------------------------------------------------------------------------
+# Gradient of the fake-quant: clipped straight-through mask
+# --------------------------------------------------------------------------
+def read_pairs(name):
+    xs, ms = [], []
+    for line in open(os.path.join(GOLD, name)):
+        line = line.split("#")[0].strip()
+        if line:
+            a, b = line.split()
+            xs.append(float(a))
+            ms.append(int(b))
+    return xs, ms
+
+
+def test_ste_mask_worked_scale(orc):
+    """At the worked example's combined scale 24 the saturation edge lies at
+    6 x 24 = 144 (tests/golden/ste_saturation.txt, worked by hand)."""
+    xs, want = read_pairs("ste_saturation.txt")
+    assert np.float32(144) * (np.float32(1) / np.float32(24)) == np.float32(6)
+    n = 16 * (-(-len(xs) // 16))
+    x = np.zeros(n, np.uint16)
+    x[: len(xs)] = bf16_bits(xs)
+    scales = np.full(n // 16, 0x5C, np.uint8)
+    assert orc.e4m3_value(0x5C) == 24.0
+    m = orc.ste_mask(x, np.float32([1.0]), scales)
+    assert list(m[: len(xs)]) == want
+    gy = np.arange(1, n + 1, dtype=np.float32)
+    gx = orc.ste_grad(x, np.float32([1.0]), scales, gy)
+    assert np.array_equal(gx[: len(xs)], np.where(np.array(want) == 1, gy[: len(xs)], 0))
+
+
+@pytest.mark.parametrize("code,g", [(0x40, 0.5), (0x08, 2.0 ** -4), (0x48, 2.0 ** -40)])
+def test_ste_mask_bruteforce_exact_scales(orc, code, g):
+    """Combined scales that are powers of two (2 x 0.5 = 1, 2^-6 x 2^-4 =
+    2^-10, 4 x 2^-40 = 2^-38) have exact reciprocals, so v = x * inv is exact
+    and the mask must equal |x| <= 6 c over every finite bf16 value, compared
+    in double: the closed form of the saturation edge."""
+    vals = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    xf = bits_to_f32(vals.astype(np.uint32) << 16)
+    vals = vals[np.isfinite(xf)]
+    vals = np.concatenate([vals, vals[: (-vals.size) % 16]])
+    c = orc.e4m3_value(code) * g
+    assert c == 2.0 ** round(np.log2(c))
+    m = orc.ste_mask(vals, np.float32([g]), np.full(vals.size // 16, code, np.uint8))
+    want = np.abs(bits_to_f32(vals.astype(np.uint32) << 16).astype(np.float64)) <= 6.0 * c
+    assert np.array_equal(m.astype(bool), want)
+
+
+def test_ste_mask_zero_scale_and_groups(orc):
+    """A zero combined scale (an all-zero group, g = 0) normalises every
+    element to 0: the gradient passes everywhere.  With several groups each
+    block takes its own group's g (the same block, scale code 0x40, passes
+    under g = 0.5 and saturates under g = 2^-10 for x = 3)."""
+    x = bf16_bits([3.0] * 32)
+    m = orc.ste_mask(x, np.float32([0.0]), np.full(2, 0x40, np.uint8))
+    assert m.all()
+    m = orc.ste_mask(x, np.float32([0.5, 2.0 ** -10]), np.full(2, 0x40, np.uint8), G=2)
+    assert m[:16].all() and not m[16:].any()
+
+
+def test_ste_mask_marks_exactly_the_saturated_outputs(orc):
+    """Training values spread wider than the rollout's (relative noise 0.3
+    instead of 0.01) often leave the rollout's block range.  Where the mask is
+    0, the guided forward saturates: its code has magnitude index 7, its
+    output is 6 s g (rounded to bf16) and stays there when |x| grows by one
+    bf16 step.  The mask reads the same scales from the guidance stream's
+    scale plane as from the scale array."""
+    rng = np.random.default_rng(5)
+    n = 16 * 4096
+    yf = (rng.standard_normal(n) * np.exp(rng.uniform(-2, 2, n))).astype(np.float32)
+    y = bf16_bits(yf)
+    xf = bits_to_f32(y.astype(np.uint32) << 16) * (1 + 0.3 * rng.standard_normal(n)).astype(np.float32)
+    x = bf16_bits(xf)
+    g, _ = orc.amax(y)
+    codes, scales, gd = orc.quant_rollout(y, g, 2)
+    m = orc.ste_mask(x, g, gd)                   # the guidance stream's scale plane
+    assert np.array_equal(m, orc.ste_mask(x, g, scales))
+    assert 0 < (m == 0).sum() < n // 10
+    yg, cg = orc.fakequant_guided(x, g, gd, 2)
+    nib = orc.unpack_nibbles(cg)
+    sat = m == 0
+    assert np.all((nib[sat] & 7) == 7)
+    # one bf16 step away from zero keeps a saturated output where it is
+    x_up = (x.astype(np.int32) + 1).astype(np.uint16)
+    x_up[~sat] = x[~sat]
+    yg_up, _ = orc.fakequant_guided(x_up, g, gd, 2)
+    assert np.array_equal(yg_up[sat], yg[sat])
+    # and that output is 6 s g, rounded to bf16 (fp32 product, then bf16)
+    s_val = np.array([orc.e4m3_value(int(c)) for c in scales], np.float32)[np.arange(n) // 16]
+    want = torch.from_numpy((np.float32(6.0) * s_val[sat]) * g[0]).to(torch.bfloat16).view(torch.int16)
+    assert np.array_equal(yg[sat] & 0x7FFF, want.numpy().view(np.uint16))

@@ -504,37 +504,139 @@ def test_graph_replay_matches_eager(tq):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
 
 
-def test_qat_autograd_wrappers(tq):
-    """Forward = the kernels (already pinned to the oracle above); backward =
-    the incoming gradient, unchanged (straight-through)."""
+def _saturating_pair(n, seed):
+    """A training tensor much wider than its rollout copy (relative noise 0.3),
+    so that many training values leave the rollout's block range and the
+    forward saturates there."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(n) * np.exp(rng.uniform(-2, 2, n))
+    Y, X = _pair_from_np(x, 0.3, seed)          # X = the noisy copy: the wider one
+    return X, Y
+
+
+def _bf16_grad(n, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("ste", ["clipped", "identity"])
+def test_qat_autograd_wrappers(tq, ste):
+    """Each autograd wrapper against the oracle: the forward equals the
+    oracle's fake-quant bit for bit (guided, full code, shared-scale RTN,
+    own-scale RTN with a given g, and plain QAT with its own scales on both
+    kernel paths, G = 1 and 4); the backward equals the oracle's clipped
+    straight-through gradient (gy where |v| <= 6, +0 where the forward
+    saturated) or gy itself with ste="identity".  The wrappers get the
+    oracle's global scales and guidance as inputs, so every expected value
+    comes from the oracle alone."""
     from precision_numerics_block_amd import qat
 
-    X, Y = synth.make_pair(1, 0, (256, 2048), DEV)
-    g = tq.amax(Y)
-    codes, scales, gd2 = tq.quant_rollout(Y, g, 2)
-    gd4 = tq.guidance_pack(codes, scales, X.numel(), 4)
-    gx = tq.amax(X)
-    cases = [
-        (lambda x: qat.guided_fake_quant(x, g, gd2, 2), lambda: tq.fakequant_guided(X, g, gd2, 2)[0]),
-        (lambda x: qat.fullcode_fake_quant(x, g, gd4), lambda: tq.fakequant_fullcode(X, g, gd4)[0]),
-        (lambda x: qat.rtn_fake_quant(x, gx), lambda: tq.fakequant_rtn(X, gx)[0]),
-        (lambda x: qat.rtn_fake_quant(x, g, scales), lambda: tq.fakequant_rtn(X, g, scales)[0]),
-        (lambda x: qat.own_scale_fake_quant(x), lambda: tq.fakequant_rtn(X, gx)[0]),
-        (lambda x: qat.own_scale_fake_quant(x, 4), lambda: tq.fakequant_rtn(X, tq.amax(X, 4), None, 4)[0]),
-    ]
-    for fwd, ref in cases:
+    n = 16 * 8192
+    X, Y = _saturating_pair(n, 77)
+    Xh, Yh = h16(X), h16(Y)
+    og, _ = oracle.amax(Yh)
+    oc, os_, ogd2 = oracle.quant_rollout(Yh, og, 2)
+    ogd4 = oracle.guidance_pack(oc, os_, n, 4)
+    ogx, _ = oracle.amax(Xh)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    g, gd2, gd4, sc, gx = dev(og), dev(ogd2), dev(ogd4), dev(os_), dev(ogx)
+    cases = [("guided k=2", lambda x: qat.guided_fake_quant(x, g, gd2, 2, ste=ste),
+              oracle.fakequant_guided(Xh, og, ogd2, 2)[0], og, os_, 1),
+             ("full code", lambda x: qat.fullcode_fake_quant(x, g, gd4, ste=ste),
+              oracle.fakequant_fullcode(Xh, og, ogd4)[0], og, os_, 1),
+             ("rtn shared scales", lambda x: qat.rtn_fake_quant(x, g, sc, ste=ste),
+              oracle.fakequant_rtn(Xh, og, os_)[0], og, os_, 1)]
+    oy, _, own = oracle.fakequant_rtn(Xh, ogx, None)
+    cases.append(("rtn own scales", lambda x: qat.rtn_fake_quant(x, gx, ste=ste), oy, ogx, own, 1))
+    for G in (1, 4):
+        ogG, _ = oracle.amax(Xh, G)
+        oyG, _, ownG = oracle.fakequant_rtn(Xh, ogG, None, G)
+        for path in qat.PATHS:
+            cases.append((f"own scales G={G} {path}",
+                          lambda x, G=G, path=path: qat.own_scale_fake_quant(x, G, path=path, ste=ste),
+                          oyG, ogG, ownG, G))
+    saturated = 0
+    for i, (what, fwd, want_y, og_, osc, G) in enumerate(cases):
         x = X.clone().requires_grad_(True)
         y = fwd(x)
-        assert torch.equal(y.view(torch.int16), ref().view(torch.int16))
-        gy = torch.randn_like(y)
+        assert_eq(h16(y), want_y, f"{what}: forward")
+        gy = _bf16_grad(n, 100 + i)
         y.backward(gy)
-        assert torch.equal(x.grad, gy)
+        want_g = h16(gy)
+        if ste == "clipped":
+            want_g = oracle.ste_grad(Xh, og_, osc, h16(gy), G)
+            saturated += int((oracle.ste_mask(Xh, og_, osc, G) == 0).sum())
+        assert_eq(h16(x.grad), want_g, f"{what}: gradient")
+    if ste == "clipped":
+        assert saturated > 100, "the case must exercise the clipped gradient"
     # a tiny training step through the guided fake-quant
     w = torch.randn(2048, 64, device=DEV, dtype=torch.float32, requires_grad=True)
-    x = X.clone().requires_grad_(True)
-    loss = (qat.guided_fake_quant(x, g, gd2, 2).float() @ w).square().mean()
+    x = X.reshape(-1, 2048).clone().requires_grad_(True)
+    loss = (qat.guided_fake_quant(x, g, gd2, 2, ste=ste).float() @ w).square().mean()
     loss.backward()
     assert torch.isfinite(w.grad).all() and x.grad is not None and torch.isfinite(x.grad.float()).all()
+
+
+def test_qat_onepass_recovers_from_barrier_timeout(tq, monkeypatch):
+    """Plain QAT on the one-pass path with the grid barrier forced to give
+    up (a zero time limit set from the host): the wrapper reads the status
+    word, warns, and recomputes through the two-kernel path; the result is
+    the oracle's, and the work buffer is zeroed for the next call."""
+    from precision_numerics_block_amd import qat
+
+    X, _ = synth.make_pair(2, 0, (8, 512, 2048), DEV)
+    work = torch.zeros(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
+    monkeypatch.setenv("TRACE_ONEPASS_WAIT_US", "0")
+    with pytest.warns(RuntimeWarning, match="timed out"):
+        y = qat.own_scale_fake_quant(X, 1, work=work, path="onepass")
+    monkeypatch.delenv("TRACE_ONEPASS_WAIT_US")
+    torch.cuda.synchronize()
+    assert bool((work == 0).all())
+    Xh = h16(X)
+    og, _ = oracle.amax(Xh)
+    assert_eq(h16(y), oracle.fakequant_rtn(Xh, og, None)[0], "recomputed forward")
+    y2 = qat.own_scale_fake_quant(X, 1, work=work, path="onepass")
+    assert_eq(h16(y2), h16(y), "the next one-pass call")
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_ste_grad_bruteforce(tq, f32):
+    """trace_fakequant_ste_grad over every finite bf16 value (anchored
+    blocks) with block scales drawn over the whole E4M3 range and global
+    scales over many binades (one group per block), against the oracle;
+    bf16 and f32 gradients, and in place (gx = gy)."""
+    Xh = anchored_blocks()
+    n = Xh.size
+    nblk = n // 16
+    rng = np.random.default_rng(41 + f32)
+    scales = rng.integers(0, 127, nblk).astype(np.uint8)
+    g = (2.0 ** rng.uniform(-40, 20, nblk)).astype(np.float32)
+    g[::97] = 0.0
+    X = to_dev_bf16(Xh)
+    gy = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(DEV)
+    if not f32:
+        gy = gy.to(torch.bfloat16)
+    gd, sd = torch.from_numpy(g).to(DEV), torch.from_numpy(scales).to(DEV)
+    gx = tq.fakequant_ste_grad(X, gd, sd, gy, nblk)
+    gy_np = gy.cpu().numpy() if f32 else h16(gy)
+    want = oracle.ste_grad(Xh, g, scales, gy_np, nblk)
+    got = gx.cpu().numpy() if f32 else h16(gx)
+    assert_eq(got.view(np.uint32) if f32 else got, want.view(np.uint32) if f32 else want, "ste grad")
+    m = oracle.ste_mask(Xh, g, scales, nblk)
+    assert 0.05 < (m == 0).mean() < 0.95, "both sides of the edge must be covered"
+    tq.fakequant_ste_grad(X, gd, sd, gy, nblk, out=gy)          # in place
+    got = gy.cpu().numpy() if f32 else h16(gy)
+    assert_eq(got.view(np.uint32) if f32 else got, want.view(np.uint32) if f32 else want, "in place")
+    # one group, ragged sizes
+    for nb in (1, 37, 513 * 4 + 3):
+        Xs = Xh[: 16 * nb]
+        gs = np.float32([2.0 ** -7])
+        ss = scales[:nb]
+        gy_s = torch.from_numpy(rng.standard_normal(16 * nb).astype(np.float32)).to(DEV)
+        got = tq.fakequant_ste_grad(to_dev_bf16(Xs), torch.from_numpy(gs).to(DEV), torch.from_numpy(ss).to(DEV),
+                                    gy_s).cpu().numpy()
+        want = oracle.ste_grad(Xs, gs, ss, gy_s.cpu().numpy())
+        assert_eq(got.view(np.uint32), want.view(np.uint32), f"one group, {nb} blocks")
 
 
 @pytest.mark.parametrize("wl", [3, 4, 5])
@@ -807,8 +909,9 @@ def test_onepass_graph_replay_matches_eager(tq):
 def test_onepass_barrier_timeout_reported(tq, monkeypatch):
     """The failure path of the bounded grid barrier, forced from the host with
     a zero time limit: the workgroups that wait give up, every kernel exits,
-    and the status word reports TRACE_E_BARRIER.  The work buffer is then
-    zero-filled again, as the contract asks, and a normal call is exact."""
+    and the status word reports TRACE_E_BARRIER.  Every workgroup still counts
+    out, so the work buffer comes back zeroed, and the next calls on the same
+    buffer (rollout, then own-scale RTN, with no fill in between) are exact."""
     X, Y = synth.make_pair(2, 0, (8, 512, 2048), DEV)
     work = torch.zeros(tq.onepass_work_bytes(1), dtype=torch.uint8, device=DEV)
     st = torch.zeros(4, dtype=torch.int32, device=DEV)
@@ -816,8 +919,13 @@ def test_onepass_barrier_timeout_reported(tq, monkeypatch):
     tq.quant_rollout_onepass(Y, 2, status=st, work=work)
     torch.cuda.synchronize()
     assert int(st[0]) == -10
+    assert bool((work == 0).all()), "a timed-out call leaves the work buffer zeroed"
+    st.zero_()
+    tq.fakequant_rtn_onepass(X, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -10
+    assert bool((work == 0).all()), "a timed-out RTN call leaves the work buffer zeroed"
     monkeypatch.delenv("TRACE_ONEPASS_WAIT_US")
-    work.zero_()
     st.zero_()
     g, codes, scales, gd = tq.quant_rollout_onepass(Y, 2, status=st, work=work)
     torch.cuda.synchronize()
@@ -827,6 +935,34 @@ def test_onepass_barrier_timeout_reported(tq, monkeypatch):
     assert_eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
     assert_eq(h8(codes), oc, "codes")
     assert_eq(h8(gd), ogd, "guidance")
+    gx, y, _, _ = tq.fakequant_rtn_onepass(X, status=st, work=work)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 0 and bool((work == 0).all())
+    ogx, _ = oracle.amax(h16(X))
+    oy, _, _ = oracle.fakequant_rtn(h16(X), ogx, None, 1, False)
+    assert_eq(gx.cpu().numpy().view(np.uint32), ogx.view(np.uint32), "rtn g")
+    assert_eq(h16(y), oy, "rtn y")
+
+
+@pytest.mark.parametrize("cap", [1, 2, 5])
+def test_onepass_many_groups_per_workgroup(tq, cap):
+    """More groups in one workgroup's run of items than its 128 LDS slots of
+    global scales (3000 groups of one block, 1500 of two, 375 of eight, over
+    1, 2 or 5 workgroups): groups past the slots take the per-item read of the
+    group maxima, which every wave must finish before its workgroup counts
+    out and the last one out clears them.  Rollout at every k and own-scale
+    RTN in bf16 and f32, against the oracle."""
+    rng = np.random.default_rng(300 + cap)
+    nblk = 3000
+    x = rng.standard_normal(16 * nblk) * np.exp(rng.uniform(-3, 3, 16 * nblk))
+    X, Y = _pair_from_np(x, 0.01, nblk + cap)
+    for G in (nblk, nblk // 2, nblk // 8):
+        for k in (1, 2, 3, 4):
+            c = Checker(tq, X, Y, k, G, onepass=cap)
+            c.run_gpu(out_f32=False)
+            c.check()
+        for out_f32 in (False, True):
+            check_rtn_onepass(tq, X, G, cap, out_f32)
 
 
 # ---------------------------------------------------------------------------
