@@ -1,9 +1,11 @@
 """Benchmark of the rollout-guided FP4 fake-quant hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of a workload.  For each
-tensor of the workload (default: routed-expert activations 64 experts x 512
-tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
-0.01, k = 2 guidance bits):
+tensor of the workload (default: the batched MoE step, routed-expert
+activations 128 experts x 1024 tokens x 4096 hidden, Student-t(3), plus one
+KV layer, K and V 65536 tokens x 8 heads x 128, in one [2, T, H, D] buffer
+with one global scale each; bf16, rollout copies with relative noise 0.01,
+k = 2 guidance bits):
 
   rollout   amax(Y) + RTN quantise + guidance (k): the one-pass kernel (one
             read of Y) when one global-scale group fits on chip (one launch
@@ -14,15 +16,18 @@ tokens x 2048 hidden, bf16, Student-t(4), rollout copy with relative noise
             group fits on chip, else the two kernels)
 
 `value` is the whole step's algorithmic bytes per second (GB/s) over K timed
-steps, replayed from a HIP graph.  Algorithmic bytes: every operation of the
-step reads its inputs once and writes its outputs once (16.875 B per element
-at k = 2); a separate amax pass re-reads its input and is not counted there,
-only on its own per-kernel line.  `roofline` is the guided fake-quant kernel
-(the metric's subject) against the 8 TB/s HBM peak, its launch duration timed
-with HIP events on the stream it runs on over K back-to-back launches;
-`kernels` gives the same for every step kernel; `mismatch` holds the
-train/rollout code-mismatch rates; `cpu_baseline` is the CPU oracle on a
-bounded sample of the same step.
+steps, replayed from a HIP graph (`value_is` says so in the output).
+Algorithmic bytes: every operation of the step reads its inputs once and
+writes its outputs once (16.875 B per element at k = 2); a separate amax pass
+re-reads its input and is not counted there, only on its own per-kernel line.
+`roofline` is the guided fake-quant kernel (the metric's subject) on the
+workload's first tensor (one launch of k_fakequant_guided<k, one group>),
+against the 8 TB/s HBM peak, its launch duration timed with HIP events on the
+stream it runs on over K back-to-back launches; `guided_fakequant` gives the
+same for every tensor of the workload; `kernels` gives it for every step
+kernel; `mismatch` holds the train/rollout code-mismatch rates;
+`cpu_baseline` is the CPU oracle on a bounded sample of the same step (a
+slice of every tensor, in proportion to its size).
 
     python bench.py [--steps K] [--warmup W] [--workload 1..5] [--k 1|2] [--no-cpu]
 """
@@ -37,14 +42,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = 2
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_expert_act_64x512x2048.txt")
+DEFAULT_WORKLOAD = 5
+# HBM counter summary of the roofline kernel, per default-workload launch
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_fakequant_guided_k2_moe_act_128x1024x4096.txt")
 KERNEL_SRC = os.path.join(ROOT, "precision_numerics_block_amd", "csrc", "trace_quant.hip")
 
 STEP = ["rollout", "guidance_pack_full", "fakequant_guided", "fakequant_fullcode", "qat_rtn_own"]
 # per-kernel lines: the step's launches, and both paths of each fused pair on their own
 KERNELS = STEP + ["rollout_onepass", "amax_rollout", "quant_rollout", "rtn_onepass", "amax_training",
-                  "fakequant_rtn_own"]
+                  "fakequant_rtn_own", "fakequant_ste_grad"]
+ROOF = "fakequant_guided@0"            # the roofline line: the guided kernel on the first tensor alone
 
 
 def parse():
@@ -85,6 +92,7 @@ def bytes_per_elem(k):
         "fakequant_rtn_own": 2.0 + 2.0,
         "qat_rtn_own": 2.0 + 2.0,
         "rtn_onepass": 2.0 + 2.0,
+        "fakequant_ste_grad": 2.0 + 1 / 16 + 2.0 + 2.0,        # x, scales, gy in; gx out (bf16)
     }
 
 
@@ -115,62 +123,73 @@ def load_traffic():
         return None
 
 
-def cpu_baseline(X, Y, n_sample, k):
+def cpu_baseline(pairs, names, n_sample, k):
+    """The CPU oracle on a bounded sample of the workload: the first elements
+    of every tensor's X and Y, in proportion to the tensor's size (each slice
+    one global-scale group), through the whole step; single-threaded, then
+    on all host threads of one GPU's share."""
     import numpy as np
     import torch
 
     import oracle
 
-    h = lambda t: t.reshape(-1)[:n_sample].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa
-    Xh, Yh = h(X), h(Y)
-    n = Xh.size
+    ns = [X.numel() for X, _ in pairs]
+    take = [max(16, n_sample * n // sum(ns) // 16 * 16) for n in ns]
+    h = lambda t, m: t.reshape(-1)[:m].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa
+    samples = [(h(X, m), h(Y, m)) for (X, Y), m in zip(pairs, take)]
+    n = sum(take)
+
+    def step_one(Xh, Yh, gy, gx):
+        codes, scales, gd = oracle.quant_rollout(Yh, gy, k)
+        gd4 = oracle.guidance_pack(codes, scales, Yh.size, 4)
+        oracle.fakequant_guided(Xh, gy, gd, k, codes=False)
+        oracle.fakequant_fullcode(Xh, gy, gd4, codes=False)
+        oracle.fakequant_rtn(Xh, gx, codes=False)
+
     t0 = time.perf_counter()
-    g, _ = oracle.amax(Yh)
-    codes, scales, gd = oracle.quant_rollout(Yh, g, k)
-    gd4 = oracle.guidance_pack(codes, scales, n, 4)
-    oracle.fakequant_guided(Xh, g, gd, k, codes=False)
-    oracle.fakequant_fullcode(Xh, g, gd4, codes=False)
-    gx, _ = oracle.amax(Xh)
-    oracle.fakequant_rtn(Xh, gx, codes=False)
+    gs = []
+    for Xh, Yh in samples:
+        gy, _ = oracle.amax(Yh)
+        gx, _ = oracle.amax(Xh)
+        step_one(Xh, Yh, gy, gx)
+        gs.append((gy, gx))
     dt = time.perf_counter() - t0
     step_bytes = step_bytes_per_elem(k) * n
+    what = ", ".join(f"{m} of {nm}" for nm, m in zip(names, take))
     out = {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"first {n} elements of the first tensor's X and Y, whole step, {dt:.1f} s "
-                     f"single-threaded C"}
-    # The same oracle on all host cores of one GPU's share: the sample in
-    # contiguous slices (whole blocks), one thread per slice (ctypes releases
-    # the GIL).  The global scale is the largest of the slices' scales (the
-    # division by 2688 rounds monotonically); given it, blocks are independent.
+           "sample": f"first elements of each tensor's X and Y ({what}; {n} in all), whole step, "
+                     f"{dt:.1f} s single-threaded C"}
+    # The same oracle on all host cores of one GPU's share: each slice cut
+    # into contiguous pieces (whole blocks), one thread per piece (ctypes
+    # releases the GIL).  A slice's global scale is the largest of its
+    # pieces' scales (the division by 2688 rounds monotonically); given it,
+    # blocks are independent.
     from concurrent.futures import ThreadPoolExecutor
 
     T = min(16, os.cpu_count() or 1)
-    cut = [(n // 16) * i // T * 16 for i in range(T + 1)]
-    sl = [(Xh[a:b], Yh[a:b]) for a, b in zip(cut[:-1], cut[1:]) if b > a]
-
-    def one(xy, gy, gx):
-        xs, ys = xy
-        c, sc, gd_ = oracle.quant_rollout(ys, gy, k)
-        gd4_ = oracle.guidance_pack(c, sc, ys.size, 4)
-        oracle.fakequant_guided(xs, gy, gd_, k, codes=False)
-        oracle.fakequant_fullcode(xs, gy, gd4_, codes=False)
-        oracle.fakequant_rtn(xs, gx, codes=False)
-
+    pieces = []
+    for si, (Xh, Yh) in enumerate(samples):
+        cut = [(Xh.size // 16) * i // T * 16 for i in range(T + 1)]
+        pieces += [(si, Xh[a:b], Yh[a:b]) for a, b in zip(cut[:-1], cut[1:]) if b > a]
     with ThreadPoolExecutor(max_workers=T) as ex:
         t0 = time.perf_counter()
-        gys = list(ex.map(lambda xy: oracle.amax(xy[1])[0], sl))
-        gxs = list(ex.map(lambda xy: oracle.amax(xy[0])[0], sl))
-        gy = np.max(np.stack(gys), axis=0)
-        gx = np.max(np.stack(gxs), axis=0)
-        list(ex.map(lambda xy: one(xy, gy, gx), sl))
+        gy_p = list(ex.map(lambda p_: oracle.amax(p_[2])[0], pieces))
+        gx_p = list(ex.map(lambda p_: oracle.amax(p_[1])[0], pieces))
+        gy_s = [np.max(np.stack([g for p_, g in zip(pieces, gy_p) if p_[0] == si]), axis=0)
+                for si in range(len(samples))]
+        gx_s = [np.max(np.stack([g for p_, g in zip(pieces, gx_p) if p_[0] == si]), axis=0)
+                for si in range(len(samples))]
+        list(ex.map(lambda p_: step_one(p_[1], p_[2], gy_s[p_[0]], gx_s[p_[0]]), pieces))
         dt_t = time.perf_counter() - t0
-    assert np.array_equal(gy, g) and np.array_equal(gx, oracle.amax(Xh)[0])
+    for (gy, gx), gy2, gx2 in zip(gs, gy_s, gx_s):
+        assert np.array_equal(gy, gy2) and np.array_equal(gx, gx2)
     model = ""
     try:
         model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
     except (OSError, StopIteration):
         pass
     out["all_cores"] = {"value": round(step_bytes / dt_t / 1e9, 4), "unit": "GB/s", "cores": T,
-                        "sample": f"the same sample in {len(sl)} slices, one thread each, {dt_t:.2f} s"}
+                        "sample": f"the same sample in {len(pieces)} pieces, one thread each, {dt_t:.2f} s"}
     out["host"] = {"nproc": os.cpu_count(), "cpu_model": model}
     return out
 
@@ -228,42 +247,101 @@ def weight_stats(tq, K):
     expert weights, one global scale per expert matrix: per-kernel burst
     timing of its amax and its RTN quantiser (no guidance), the whole call,
     and the one-pass rollout without guidance, which gives the same results.
-    Algorithmic bytes read the weights once: 2 + 0.5 + 1/16 B per element."""
+    Two weight buffers alternate (as the step's input sets do), so no call
+    finds its input in the last-level cache; each line is the best of three
+    loops of K calls after 20 untimed ones.  Algorithmic bytes read the
+    weights once: 2 + 0.5 + 1/16 B per element."""
     import torch
     from precision_numerics_block_amd import synth
 
     dev = "cuda:0"
-    W = synth.make_weights(synth.WEIGHT_SHAPE, dev).reshape(-1)
+    Ws = [synth.make_weights(synth.WEIGHT_SHAPE, dev).reshape(-1)]
+    Ws.append(Ws[0].view(synth.WEIGHT_SHAPE).roll(1, 0).reshape(-1).contiguous())
     E = synth.WEIGHT_SHAPE[0]
-    n = W.numel()
+    n = Ws[0].numel()
     g = torch.empty(E, dtype=torch.float32, device=dev)
     codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
     work = torch.zeros(max(tq.onepass_work_bytes(E), 256), dtype=torch.uint8, device=dev)
-    runs = {"weight_amax": (2.0, lambda: tq.amax(W, E, out=g)),
-            "weight_quant": (2.0 + 0.5 + 1 / 16,
-                             lambda: tq.quant_rollout(W, g, 2, E, guidance=False, codes=codes, scales=scales)),
-            "quant_weight": (2.0 + 0.5 + 1 / 16, lambda: tq.quant_weight(W, E, g=g, codes=codes, scales=scales)),
+    b = 2.0 + 0.5 + 1 / 16
+    runs = {"weight_amax": (2.0, lambda W: tq.amax(W, E, out=g)),
+            "weight_quant": (b, lambda W: tq.quant_rollout(W, g, 2, E, guidance=False, codes=codes, scales=scales)),
+            "quant_weight": (b, lambda W: tq.quant_weight(W, E, g=g, codes=codes, scales=scales)),
             # the same results from one read of the weights: every matrix fits on chip, so the one-pass
             # rollout without guidance runs one launch per block of matrices
-            "quant_weight_onepass": (2.0 + 0.5 + 1 / 16,
-                                     lambda: tq.quant_rollout_onepass(W, 2, E, g=g, guidance=False, codes=codes,
-                                                                      scales=scales, work=work))}
-    out = {"workload": f"expert weights {'x'.join(map(str, synth.WEIGHT_SHAPE))} bf16, G={E} (one per matrix)"}
+            "quant_weight_onepass": (b, lambda W: tq.quant_rollout_onepass(W, 2, E, g=g, guidance=False,
+                                                                           codes=codes, scales=scales, work=work))}
+    out = {"workload": f"expert weights {'x'.join(map(str, synth.WEIGHT_SHAPE))} bf16, G={E} (one per matrix), "
+                       "two buffers alternating"}
     for nm, (bpe, fn) in runs.items():
-        for _ in range(5):              # freshly allocated buffers: the first calls run slower
-            fn()
+        for i in range(20):
+            fn(Ws[i % 2])
         torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(K):
+                fn(Ws[i % 2])
+            e.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(e) / K
+            best = ms if best is None else min(best, ms)
+        gbs = bpe * n / (best * 1e-3) / 1e9
+        out[nm] = {"us": round(best * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del Ws
+    return out
+
+
+def per_expert_stats(tq, sets, bufs, names_shapes, K, k):
+    """The activation tensor with one global scale per expert (G = experts,
+    the reported variant of the global-scale grouping): every expert fits on
+    chip, so the one-pass entry points read it once, one launch per block of
+    experts that fits; against amax + the streaming kernel.  Per-kernel burst
+    timing over K launches on alternating input sets."""
+    import torch
+
+    name, shape = names_shapes[0]
+    E = shape[0]
+    n = sets[0][0][0].numel()
+    dev = sets[0][0][0].device
+    g = torch.empty(E, dtype=torch.float32, device=dev)
+    work = torch.zeros(tq.onepass_work_bytes(E), dtype=torch.uint8, device=dev)
+    st = torch.zeros(4, dtype=torch.int32, device=dev)
+    rb = 2.0 + 0.5 + 1 / 16 + (1 / 16 + k / 8)
+
+    def run(nm, i):
+        (X, Y), b = sets[i % 2][0], bufs[i % 2][0]
+        if nm == "rollout_onepass":
+            tq.quant_rollout_onepass(Y, k, E, g=g, guidance=b["gd"], codes=b["codes"], scales=b["scales"],
+                                     work=work, status=st)
+        elif nm == "rollout_two_kernel":
+            tq.amax(Y, E, out=g)
+            tq.quant_rollout(Y, g, k, E, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
+        elif nm == "qat_rtn_onepass":
+            tq.fakequant_rtn_onepass(X, E, g=g, out=b["y_r"], work=work, status=st)
+        else:
+            tq.amax(X, E, out=g)
+            tq.fakequant_rtn(X, g, None, E, out=b["y_r"])
+
+    out = {"tensor": f"{name} {'x'.join(map(str, shape))}, G={E} (one global scale per expert)"}
+    for nm, bpe in (("rollout_onepass", rb), ("rollout_two_kernel", rb), ("qat_rtn_onepass", 4.0),
+                    ("qat_rtn_two_kernel", 4.0)):
+        for i in range(4):
+            run(nm, i)
         a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(K):
-            fn()
+        for i in range(K):
+            run(nm, i)
         e.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(e) / K
         gbs = bpe * n / (ms * 1e-3) / 1e9
         out[nm] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    del W
+    if int(st[0].item()) != 0:
+        raise RuntimeError(f"per-expert one-pass status {int(st[0].item())}")
+    out["onepass_speedup"] = {"rollout": round(out["rollout_two_kernel"]["us"] / out["rollout_onepass"]["us"], 3),
+                              "qat_rtn": round(out["qat_rtn_two_kernel"]["us"] / out["qat_rtn_onepass"]["us"], 3)}
     return out
 
 
@@ -520,8 +598,12 @@ def main():
             tq.quant_rollout(Y, b["g"], k, G, guidance=b["gd"], codes=b["codes"], scales=b["scales"])
 
     def launch(nm, i):
-        """Kernel `nm` once on every tensor of input set i % 2."""
-        for (X, Y), b, n, G, one in zip(sets[i % 2], bufs[i % 2], ns, Gs, onepass):
+        """Kernel `nm` once on every tensor of input set i % 2 (`nm@t`: on
+        tensor t alone)."""
+        nm, _, only = nm.partition("@")
+        for t, ((X, Y), b, n, G, one) in enumerate(zip(sets[i % 2], bufs[i % 2], ns, Gs, onepass)):
+            if only and t != int(only):
+                continue
             if nm == "rollout":
                 rollout(Y, b, G, one)
             elif nm == "rollout_onepass":
@@ -542,6 +624,8 @@ def main():
                 tq.fakequant_fullcode(X, b["g"], b["gd4"], G, out=b["y_f"])
             elif nm == "amax_training":
                 tq.amax(X, G, out=b["gx"])
+            elif nm == "fakequant_ste_grad":            # the guided leg's backward, gy = its output
+                tq.fakequant_ste_grad(X, b["g"], b["gd"], b["y_g"], G, out=b["y_f"])
             else:
                 tq.fakequant_rtn(X, b["gx"], None, G, out=b["y_r"])
 
@@ -603,7 +687,8 @@ def main():
     # (a single launch between two events would also count the event's own
     # dispatch and release, ~2-4 us)
     per = {}
-    for nm in KERNELS:
+    guided_each = [f"fakequant_guided@{t}" for t in range(len(pairs))] if len(pairs) > 1 else [ROOF]
+    for nm in KERNELS + guided_each:
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(K):
@@ -615,9 +700,18 @@ def main():
     bpe = bytes_per_elem(k)
     step_bytes = step_bytes_per_elem(k) * n_total
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    g_ms = per["fakequant_guided"]
-    g_bytes = bpe["fakequant_guided"] * n_total
+    g_ms = per[ROOF]                                    # the first tensor's guided launch
+    g_bytes = bpe["fakequant_guided"] * ns[0]
     achieved = g_bytes / (g_ms * 1e-3) / 1e9
+    guided = {}
+    for t, nm in enumerate(guided_each):
+        gb = bpe["fakequant_guided"] * ns[t]
+        guided[f"{names_shapes[t][0]} {'x'.join(map(str, names_shapes[t][1]))} G={Gs[t]}"] = {
+            "us": round(per[nm] * 1e3, 2), "GBps": round(gb / (per[nm] * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(gb / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    gall = bpe["fakequant_guided"] * n_total / (per["fakequant_guided"] * 1e-3) / 1e9
+    guided["all tensors"] = {"us": round(per["fakequant_guided"] * 1e3, 2), "GBps": round(gall, 1),
+                             "frac_of_peak": round(gall / HBM_PEAK_GBS, 4)}
     kernels = {nm: {"us": round(per[nm] * 1e3, 2),
                     "GBps": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -653,6 +747,9 @@ def main():
     variants = None if args.no_variants else variant_stats(tq, sets, bufs, ns, Gs, min(K, 20), k)
     mx = None if args.no_variants else mx_stats(tq, sets, ns, min(K, 20), k)
     weights = None if args.no_variants else weight_stats(tq, min(K, 20))
+    experts = None
+    if not args.no_variants and names_shapes[0][0] == "act":
+        experts = per_expert_stats(tq, sets, bufs, names_shapes, min(K, 20), k)
     step(0)
     mism = mismatch_stats(tq, sets[0], bufs[0], k, Gs)
     torch.cuda.synchronize()
@@ -660,8 +757,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        X, Y = pairs[0]
-        cpu = cpu_baseline(X, Y, min(args.cpu_elems, ns[0]), k)
+        cpu = cpu_baseline(pairs, [nm for nm, _ in names_shapes], min(args.cpu_elems, n_total), k)
 
     default = args.workload == DEFAULT_WORKLOAD and k == 2
     dist = {"normal_outliers": "N(0,1), 0.5% x20", "student_t4": "Student-t nu=4",
@@ -671,6 +767,8 @@ def main():
         "metric": "guided FP4 fake-quant GB/s and % of HBM peak on 1 MI355X; mismatch rate",
         "value": round(value, 1),
         "unit": "GB/s",
+        "value_is": f"whole rollout+training step: {step_bytes_per_elem(k)} algorithmic B/element x "
+                    f"{n_total} elements / ms_per_step (the guided kernel alone: roofline, guided_fakequant)",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -683,6 +781,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtypes": {"inputs": "bf16", "outputs": "u8 (FP4 E2M1 codes, E4M3 scales, guidance bits), bf16 "
+                                                  "fake-quant values", "arithmetic": "f32 (scale chain, RTN)"},
         "data": "synthetic",
         "config": {"workload": f"{W.name} bf16 ({dist}, rollout relative noise {W.rel_noise}), k={k} "
                                f"guidance, G={max(Gs)}, whole rollout+training step",
@@ -693,19 +793,23 @@ def main():
                    "elements": n_total, "k": k, "G": max(Gs), "step_bytes": int(step_bytes)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic() if default else None,
-                     "kernel": f"k_fakequant_guided<{k},true,false> (trace_fakequant_guided, k={k}, bf16 out)",
+                     "kernel": f"k_fakequant_guided<{k},{'true' if Gs[0] == 1 else 'false'},false> "
+                               f"(trace_fakequant_guided, k={k}, bf16 out) on {names_shapes[0][0]} "
+                               f"{'x'.join(map(str, names_shapes[0][1]))}",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
+        "guided_fakequant": guided,
         "copy_reference": {"GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
                            "what": "torch copy_ of a 256 MiB buffer on the same GPU in the same run (runtime blit "
                                    "kernel), read + write bytes"},
         "elements_per_s": {"step": float(f"{n_total / (ms_step * 1e-3):.4g}"),
-                           "fakequant_guided": float(f"{n_total / (g_ms * 1e-3):.4g}")},
+                           "fakequant_guided": float(f"{n_total / (per['fakequant_guided'] * 1e-3):.4g}")},
         "cpu_baseline": cpu,
         "mismatch": mism,
         "kernels": kernels,
         "guidance_widths": variants,
         "mxfp4": mx,
         "fp4_weight": weights,
+        "per_expert_scales": experts,
         "transport": transport,
     }
     print(json.dumps(out))
