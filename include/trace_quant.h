@@ -42,9 +42,10 @@
  * Common rules for every entry point:
  *   - pointers are device pointers unless stated; the caller owns every
  *     buffer; the library never allocates device memory and keeps no state
- *     beyond a read-only kernel table and a host-side cache of device
- *     attributes (compute units, LDS size, clock rate); calls are
- *     thread-safe;
+ *     beyond a read-only kernel table, a host-side cache of device
+ *     attributes (compute units, LDS size, clock rate) and the static work
+ *     array of trace_quant_rollout_onepass_noalloc; calls are thread-safe
+ *     (that entry point's calls must still be ordered per device);
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns at once; outputs are valid once the stream has
  *     reached that point;
@@ -76,8 +77,10 @@ typedef enum {
     TRACE_E_NONFINITE = -7, /* (device status word) an input was inf/NaN */
     TRACE_E_FORMAT = -8,    /* a guidance record fails its header or hash check */
     TRACE_E_IO = -9,        /* a file could not be opened, written or read */
-    TRACE_E_BARRIER = -10   /* (device status word) the one-pass rollout's workgroups
+    TRACE_E_BARRIER = -10,  /* (device status word) the one-pass rollout's workgroups
                                were not all resident at once; outputs undefined */
+    TRACE_E_SCRATCH = -11   /* G exceeds the static scratch of the allocation-free
+                               one-pass rollout (4096 groups) */
 } trace_status;
 
 typedef enum { TRACE_OUT_BF16 = 0, TRACE_OUT_F32 = 1 } trace_out_dtype;
@@ -176,6 +179,24 @@ int64_t trace_onepass_capacity(int max_workgroups);
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);
+
+/* The same one-pass rollout for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no work-buffer argument; its work buffer is a static array of
+ * the library, 25 088 bytes per device (barrier counters and up to 4096
+ * group maxima), held by each device the library runs on until the process
+ * ends.  The first call on a device looks up that device's copy and enqueues
+ * one clear of it on `stream` before its launch; every call leaves it zeroed
+ * (as trace_quant_rollout_onepass does its work buffer).  All other arguments,
+ * results and status words are those of trace_quant_rollout_onepass.
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (different streams, or different host threads without
+ * ordering) race on it and give undefined results; order them on one stream.
+ * Returns TRACE_E_SCRATCH, with nothing enqueued, when G > 4096.  Allocates
+ * nothing: no hipMalloc, hipFree or allocating library call. */
+int trace_quant_rollout_onepass_noalloc(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                        uint8_t *scales, uint8_t *guidance, int max_workgroups, int *status_dev,
+                                        void *stream);
 
 /* One-pass plain QAT fake-quant with own scales: the results of trace_amax
  * on x followed by trace_fakequant_rtn with scales_in = NULL (bit for bit),

@@ -842,6 +842,18 @@ constexpr uint32_t kOpAccWord = 2 * (kOpSubgroups + 1) * kOpLine;
 constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
 constexpr uint32_t kOpTabSlots = 4;                // groups with scale tables, several-group rollout
 
+// Groups the allocation-free one-pass entry point accepts: its work buffer
+// (barrier trees and group maxima, the layout above) is the static array
+// `scratch` below, one copy per device.
+constexpr int kScratchMaxGroups = 4096;
+constexpr uint32_t kScratchWords = kOpAccWord + kScratchMaxGroups;   // 25 088 bytes
+
+}  // namespace
+
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+namespace {
+
 struct OnePass {
     const u32x4 *y;         // the input (the rollout's y, or the training tensor x)
     uint32_t cpg;           // chunks per group
@@ -2207,6 +2219,41 @@ int rollout_onepass_run(const void *y_bf16, int64_t n, int G, int k, float *g_ou
     return TRACE_OK;
 }
 
+// The device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and cleared once, in stream order before
+// the first launch that uses it.  In host code `scratch` names a host-side
+// stand-in, so only the looked-up address is ever passed to a kernel.
+int scratch_for_device(hipStream_t st, void *&out)
+{
+    static void *addr[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    static bool cleared[kMaxDevices];
+    static std::mutex clear_mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TRACE_E_HIP;
+    std::call_once(once[dev], [dev] {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+            addr[dev] = p;
+    });
+    (void)hipGetLastError();
+    if (!addr[dev])
+        return TRACE_E_HIP;
+    {
+        std::lock_guard<std::mutex> lk(clear_mu);
+        if (!cleared[dev]) {
+            hipLaunchKernelGGL(k_amax_clear, dim3((kScratchWords + 255) / 256), dim3(256), 0, st,
+                               static_cast<uint32_t *>(addr[dev]), (int)kScratchWords);
+            if (hipGetLastError() != hipSuccess)
+                return TRACE_E_HIP;
+            cleared[dev] = true;
+        }
+    }
+    out = addr[dev];
+    return TRACE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2218,6 +2265,23 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
     int rc = rollout_onepass_check(y_bf16, n, G, k, g_out, codes, scales, guidance, true, work, max_workgroups,
                                    status_dev);
     if (rc != TRACE_OK)
+        return rc;
+    return rollout_onepass_run(y_bf16, n, G, k, g_out, codes, scales, guidance, work, max_workgroups, status_dev,
+                               (hipStream_t)stream);
+}
+
+int trace_quant_rollout_onepass_noalloc(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                                        uint8_t *scales, uint8_t *guidance, int max_workgroups, int *status_dev,
+                                        void *stream)
+{
+    int rc = rollout_onepass_check(y_bf16, n, G, k, g_out, codes, scales, guidance, false, nullptr, max_workgroups,
+                                   status_dev);
+    if (rc != TRACE_OK)
+        return rc;
+    if (G > kScratchMaxGroups)
+        return TRACE_E_SCRATCH;
+    void *work = nullptr;
+    if ((rc = scratch_for_device((hipStream_t)stream, work)) != TRACE_OK)
         return rc;
     return rollout_onepass_run(y_bf16, n, G, k, g_out, codes, scales, guidance, work, max_workgroups, status_dev,
                                (hipStream_t)stream);
@@ -2594,6 +2658,7 @@ const char *trace_status_str(int status)
     case TRACE_E_FORMAT: return "guidance record fails its header or hash check";
     case TRACE_E_IO: return "file could not be opened, written or read";
     case TRACE_E_BARRIER: return "one-pass rollout: workgroups were not all resident (grid barrier timed out)";
+    case TRACE_E_SCRATCH: return "G exceeds the 4096 groups of the allocation-free one-pass rollout's static scratch";
     default: return "unknown status";
     }
 }

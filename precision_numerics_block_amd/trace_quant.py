@@ -32,6 +32,7 @@ _SIGS = {
     "trace_onepass_work_bytes": (_sz, [_int]),
     "trace_onepass_capacity": (_i64, [_int]),
     "trace_quant_rollout_onepass": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp]),
+    "trace_quant_rollout_onepass_noalloc": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_rtn_onepass": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _vp, _vp, _int, _vp, _vp]),
     "trace_fakequant_guided": (_int, [_vp, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _vp]),
     "trace_fakequant_fullcode": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp]),
@@ -62,7 +63,8 @@ OUT_BF16, OUT_F32 = 0, 1
 
 __all__ = [
     "lib", "TraceError", "code_bytes", "scale_bytes", "guidance_bytes", "amax", "quant_rollout", "quant_weight",
-    "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass", "fakequant_rtn_onepass",
+    "onepass_work_bytes", "onepass_capacity", "quant_rollout_onepass", "quant_rollout_onepass_noalloc",
+    "fakequant_rtn_onepass",
     "guidance_pack", "fakequant_guided", "fakequant_fullcode", "fakequant_rtn", "fakequant_ste_grad", "version",
     "mx_scale_bytes", "mx_guidance_bytes", "mx_quant_rollout", "mx_fakequant_guided", "mx_fakequant_rtn",
     "record_bytes", "record_to_host", "record_seal", "record_check", "record_from_host", "record_write",
@@ -188,6 +190,27 @@ def quant_rollout_onepass(y, k, G=1, g=None, guidance=True, codes=None, scales=N
     _check("trace_quant_rollout_onepass", lib.trace_quant_rollout_onepass(
         _ptr(y), n, int(G), int(k), _ptr(g), _ptr(codes), _ptr(scales), _ptr(guidance), _ptr(work),
         int(max_workgroups), _ptr(status), _stream(dev)))
+    return g, codes, scales, guidance
+
+
+def quant_rollout_onepass_noalloc(y, k, G=1, g=None, guidance=True, codes=None, scales=None, max_workgroups=0,
+                                  status=None):
+    """quant_rollout_onepass with the library's static per-device work
+    array instead of a work buffer (G <= 4096; calls on one device must be
+    ordered on one stream).  Outputs left as None are allocated here, by
+    torch; pass them all to allocate nothing."""
+    _need(y, torch.bfloat16, "y")
+    n, dev = y.numel(), y.device
+    g = torch.empty(G, dtype=torch.float32, device=dev) if g is None else g
+    codes = _u8(n // 2, dev) if codes is None else codes
+    scales = _u8(n // 16, dev) if scales is None else scales
+    if guidance is True:
+        guidance = _u8(guidance_bytes(n, k), dev)
+    elif guidance is False:
+        guidance = None
+    _check("trace_quant_rollout_onepass_noalloc", lib.trace_quant_rollout_onepass_noalloc(
+        _ptr(y), n, int(G), int(k), _ptr(g), _ptr(codes), _ptr(scales), _ptr(guidance), int(max_workgroups),
+        _ptr(status), _stream(dev)))
     return g, codes, scales, guidance
 
 

@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "trace_quant.h")
 
-OK, E_NULL, E_SIZE, E_ALIGN, E_K, E_DTYPE = 0, -1, -2, -3, -4, -5
+OK, E_NULL, E_SIZE, E_ALIGN, E_K, E_DTYPE, E_SCRATCH = 0, -1, -2, -3, -4, -5, -11
 A = 0x100000          # a fake, 16-byte aligned "device" address (never dereferenced)
 
 
@@ -55,6 +55,7 @@ def test_sizes(tq):
     assert tq.onepass_work_bytes(1) == 8960 and tq.onepass_work_bytes(64) == 8960
     assert tq.onepass_work_bytes(65) == 9216 and tq.onepass_work_bytes(0) == 0
     assert "barrier" in tq.lib.trace_status_str(-10).decode()
+    assert "4096" in tq.lib.trace_status_str(-11).decode()
     assert "2^34" in tq.lib.trace_status_str(-2).decode()
     assert tq.mx_scale_bytes(32 * 10) == 10 and tq.mx_scale_bytes(16) == 0
     assert tq.mx_guidance_bytes(32 * 10, 2) == 256 + 80 and tq.mx_guidance_bytes(32 * 10, 5) == 0
@@ -125,6 +126,20 @@ def test_argument_errors_before_any_hip_call(tq):
     # more (32-bit output spans): rejected before the device query
     assert op(A, 1 << 33, 1, 4, A, A, A, A, A, 1, None, None) == E_SIZE        # codes: 2^30 chunks x 4 B
     assert rop(A, 1 << 30, 1, A, A, 1, None, None, A, 1, None, None) == E_SIZE  # f32 y: 2^27 chunks x 32 B
+    # the allocation-free one-pass rollout: the same checks (no work buffer),
+    # then its static scratch limit of 4096 groups, all before any HIP call
+    na = L.trace_quant_rollout_onepass_noalloc
+    assert na(A, 24, 1, 2, A, A, A, None, 0, None, None) == E_SIZE
+    assert na(A, n, 3, 2, A, A, A, None, 0, None, None) == E_SIZE
+    assert na(A, n, 1, 2, A, A, A, None, -1, None, None) == E_SIZE
+    assert na(A, 1 << 33, 1, 2, A, A, A, None, 1, None, None) == E_SIZE
+    assert na(None, n, 1, 2, A, A, A, None, 0, None, None) == E_NULL
+    assert na(A, n, 1, 2, A, None, A, None, 0, None, None) == E_NULL
+    assert na(A, n, 1, 2, A, A, A + 8, None, 0, None, None) == E_ALIGN
+    assert na(A, n, 1, 2, A, A, A, A + 4, 0, None, None) == E_ALIGN
+    assert na(A, n, 1, 0, A, A, A, None, 0, None, None) == E_K
+    assert na(A, 16 * 4097, 4097, 2, A, A, A, None, 0, None, None) == E_SCRATCH
+    assert na(A, 16 * 8192 * 3, 8192, 2, A, A, A, A, 0, None, None) == E_SCRATCH
     # MX variant
     assert L.trace_mx_quant_rollout(A, 48, 2, A, A, None, None) == E_SIZE
     assert L.trace_mx_quant_rollout(A, n, 2, None, A, None, None) == E_NULL
