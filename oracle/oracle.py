@@ -183,37 +183,52 @@ def _outbufs(n, out_f32, want_codes):
     return y, c
 
 
-def fakequant_guided(x, g, guidance, k, G=1, out_f32=False, b0=None, b1=None, codes=True):
+def _checked_out(out, n, out_f32, codes):
+    """Caller-given output arrays (filled only over the blocks processed)."""
+    y, c = out[0], out[1]
+    assert y.dtype == (np.float32 if out_f32 else np.uint16) and y.size == n and y.flags.c_contiguous
+    assert (c is None) == (not codes) and (c is None or (c.dtype == np.uint8 and c.size == n // 2))
+    return y, c
+
+
+def fakequant_guided(x, g, guidance, k, G=1, out_f32=False, b0=None, b1=None, codes=True, out=None):
+    """out: optional (y, codes) arrays to fill over blocks [b0, b1) only."""
     x = _u16(x).reshape(-1)
     n = x.size
     g = np.ascontiguousarray(g, np.float32)
     gd = np.ascontiguousarray(guidance, np.uint8)
     b0, b1 = _range(n, b0, b1)
-    y, c = _outbufs(n, out_f32, codes)
+    y, c = _outbufs(n, out_f32, codes) if out is None else _checked_out(out, n, out_f32, codes)
     lib().oracle_fakequant_guided(_p(x), n, G, _p(g), _p(gd), k, b0, b1, _p(y), int(out_f32), _p(c))
     return y, c
 
 
-def fakequant_fullcode(x, g, guidance, G=1, out_f32=False, b0=None, b1=None, codes=True):
+def fakequant_fullcode(x, g, guidance, G=1, out_f32=False, b0=None, b1=None, codes=True, out=None):
     x = _u16(x).reshape(-1)
     n = x.size
     g = np.ascontiguousarray(g, np.float32)
     gd = np.ascontiguousarray(guidance, np.uint8)
     b0, b1 = _range(n, b0, b1)
-    y, c = _outbufs(n, out_f32, codes)
+    y, c = _outbufs(n, out_f32, codes) if out is None else _checked_out(out, n, out_f32, codes)
     lib().oracle_fakequant_fullcode(_p(x), n, G, _p(g), _p(gd), b0, b1, _p(y), int(out_f32), _p(c))
     return y, c
 
 
-def fakequant_rtn(x, g, scales_in=None, G=1, out_f32=False, b0=None, b1=None, codes=True):
-    """Plain RTN fake-quant: returns (y, codes or None, scales used)."""
+def fakequant_rtn(x, g, scales_in=None, G=1, out_f32=False, b0=None, b1=None, codes=True, out=None):
+    """Plain RTN fake-quant: returns (y, codes or None, scales used).  out:
+    optional (y, codes, scales) arrays to fill over blocks [b0, b1) only."""
     x = _u16(x).reshape(-1)
     n = x.size
     g = np.ascontiguousarray(g, np.float32)
     sin = None if scales_in is None else np.ascontiguousarray(scales_in, np.uint8)
     b0, b1 = _range(n, b0, b1)
-    y, c = _outbufs(n, out_f32, codes)
-    sout = np.zeros(n // 16, np.uint8)
+    if out is None:
+        y, c = _outbufs(n, out_f32, codes)
+        sout = np.zeros(n // 16, np.uint8)
+    else:
+        y, c = _checked_out(out, n, out_f32, codes)
+        sout = out[2]
+        assert sout.dtype == np.uint8 and sout.size == n // 16
     lib().oracle_fakequant_rtn(_p(x), n, G, _p(g), _p(sin), b0, b1, _p(y), int(out_f32), _p(c), _p(sout))
     return y, c, sout
 
