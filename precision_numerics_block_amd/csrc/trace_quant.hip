@@ -826,7 +826,7 @@ __global__ void __launch_bounds__(kThreads)
 constexpr int kOpThreads = TRACE_OP_THREADS;
 constexpr int kOpTile = 2 * kOpThreads;            // chunks per tile (16 KiB of bf16)
 constexpr int kOpRegTiles = TRACE_OP_REG_TILES;
-constexpr int kOpStream = 8;                       // tiles in flight per lane when streaming
+constexpr int kOpStream = 4;                       // tiles in flight per lane when streaming
 // Work buffer (words): arrival counters of 16 subgroups of workgroups and
 // one top counter, each on its own 256-byte line (a same-address atomic costs
 // about 30 ns on MI355X, so 256 arrivals on one word serialise for ~8 us;
@@ -1039,20 +1039,43 @@ struct GroupTabs {
     int k;
 };
 
+// A block's scale code and the reciprocal of its combined scale.
+struct ScInv {
+    uint32_t sc;
+    float inv;
+};
+
+template <bool kTab>
+__device__ __forceinline__ ScInv block_scale_inv(uint32_t ab, float gv, const GroupTabs &tb)
+{
+    ScInv r;
+    if constexpr (kTab) {
+        r.sc = block_scale_tab(ab, tb.scale, tb.k);
+        r.inv = tb.inv[r.sc];
+    } else {
+        r.sc = block_scale(as_f(ab << 16), gv);
+        r.inv = inv_combined(e4m3_decode(r.sc), gv);
+    }
+    return r;
+}
+
+// The stores of quant_block, given the block's scale code and reciprocal.
+template <int K>
+__device__ __forceinline__ void quant_block_with(const Outs &o, const Item &w, const Blk &b, ScInv si);
+
 template <int K, bool kTab>
 __device__ __forceinline__ void quant_block(const Outs &o, const Item &w, const Blk &b, uint32_t ab, float gv,
                                             const GroupTabs &tb)
 {
+    quant_block_with<K>(o, w, b, block_scale_inv<kTab>(ab, gv, tb));
+}
+
+template <int K>
+__device__ __forceinline__ void quant_block_with(const Outs &o, const Item &w, const Blk &b, ScInv si)
+{
     const uint32_t cb = w.first - o.c0 + 2 * block_of_lane();   // the block's first chunk, in o's span
-    uint32_t sc;
-    float inv;
-    if constexpr (kTab) {
-        sc = block_scale_tab(ab, tb.scale, tb.k);
-        inv = tb.inv[sc];
-    } else {
-        sc = block_scale(as_f(ab << 16), gv);
-        inv = inv_combined(e4m3_decode(sc), gv);
-    }
+    const uint32_t sc = si.sc;
+    const float inv = si.inv;
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.scales, cb / 2, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, o.gds, cb / 2, 0, 0);
     const uint32_t c0 = rtn8(b.lo, inv), c1 = rtn8(b.hi, inv);
@@ -1156,6 +1179,11 @@ template <int K, bool kOneGroup, bool kSpan, int OUT = 0, bool kTab = kOneGroup 
 __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
 {
     static_assert(!kTab || OUT == 0, "scale tables serve the rollout codes only");
+    // Tiles read twice go in batches of kOpStream items (one load per chunk
+    // in flight per item); halved without span descriptors, where each item
+    // of a batch carries its own output descriptors in scalar registers.
+    // Batches of eight spilled some variants' registers to scratch memory.
+    constexpr int kBatch = kSpan ? kOpStream : kOpStream / 2;
     constexpr uint32_t kSlots = kTab ? (kOneGroup ? 1u : kOpTabSlots) : 0u;
     extern __shared__ u32x4 lds_tiles[];           // a.lds_tiles * 2 * kOpThreads chunks
     __shared__ uint32_t wmax[kOpThreads / 64];
@@ -1194,14 +1222,14 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     auto chunk_pair_max = [&](const Chunk (&x)[2]) {
         return max(chunk_amax_finite(x[0], a.status), chunk_amax_finite(x[1], a.status));
     };
-    for (uint32_t j = 0; j < nstr; j += kOpStream) {
-        Chunk x[kOpStream][2];
-        Item w[kOpStream];
-        for (int q = 0; q < kOpStream; ++q) {
+    for (uint32_t j = 0; j < nstr; j += kBatch) {
+        Chunk x[kBatch][2];
+        Item w[kBatch];
+        for (int q = 0; q < kBatch; ++q) {
             w[q] = item_at<kOneGroup>(a, i0 + j + q);
             load_item(a, w[q], j + q < nstr, x[q]);
         }
-        for (int q = 0; q < kOpStream; ++q)
+        for (int q = 0; q < kBatch; ++q)
             if (j + q < nstr)
                 fold(w[q].grp, chunk_pair_max(x[q]));
     }
@@ -1348,25 +1376,46 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
         };
         // (with span descriptors a register tile that is not live lies past the
         // run's end, outside the records, so it needs no descriptor of its own)
+        if constexpr (kTab) {
+            // Scale tables (groups of whole tiles, so span descriptors): the two
+            // dependent table reads of the next tile are issued before this
+            // tile's conversion and stores, so their LDS latency overlaps them
+            // instead of stalling each tile (2 waves per SIMD hide little).
+            static_assert(!kTab || kSpan, "scale tables come with span descriptors");
+            auto tabs_of = [&](int h) {
+                GroupTabs t = tabs_for(item_at<kOneGroup>(a, p2_reg + h).grp);
+                t.k = __builtin_amdgcn_readfirstlane(t.k);
+                return t;
+            };
+            ScInv nx = block_scale_inv<true>(hab[0], 0.0f, tabs_of(0));
     #pragma unroll
-        for (int h = 0; h < kOpRegTiles; ++h) {
-            Item w = item_at<kOneGroup>(a, p2_reg + h);
-            bool live = p2_reg + h < i0 + cnt;
-            block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live && !kTab ? gscale(w.grp) : 0.0f);
+            for (int h = 0; h < kOpRegTiles; ++h) {
+                const ScInv cur = nx;
+                if (h + 1 < kOpRegTiles)
+                    nx = block_scale_inv<true>(hab[h + 1], 0.0f, tabs_of(h + 1));
+                quant_block_with<K>(span, item_at<kOneGroup>(a, p2_reg + h), hr[h], cur);
+            }
+        } else {
+    #pragma unroll
+            for (int h = 0; h < kOpRegTiles; ++h) {
+                Item w = item_at<kOneGroup>(a, p2_reg + h);
+                bool live = p2_reg + h < i0 + cnt;
+                block_out(kSpan ? span : outs_for(w, live), w, hr[h], hab[h], live && !kTab ? gscale(w.grp) : 0.0f);
+            }
         }
         for (uint32_t j = 0; j < nlds; ++j) {
             Item w = item_at<kOneGroup>(a, p2_lds + j);
             Blk b = block_from_lds(lds_tiles, j);
             block_out(outs_for(w, true), w, b, block_amax_bits(b), kTab ? 0.0f : gscale(w.grp));
         }
-        for (uint32_t j = 0; j < nstr; j += kOpStream) {
-            Chunk x[kOpStream][2];
-            Item w[kOpStream];
-            for (int q = 0; q < kOpStream; ++q) {
+        for (uint32_t j = 0; j < nstr; j += kBatch) {
+            Chunk x[kBatch][2];
+            Item w[kBatch];
+            for (int q = 0; q < kBatch; ++q) {
                 w[q] = item_at<kOneGroup>(a, i0 + j + q);
                 load_item(a, w[q], j + q < nstr, x[q]);
             }
-            for (int q = 0; q < kOpStream; ++q) {
+            for (int q = 0; q < kBatch; ++q) {
                 bool live = j + q < nstr;
                 Blk b = to_block(x[q]);
                 block_out(outs_for(w[q], live), w[q], b, block_amax_bits(b), live && !kTab ? gscale(w[q].grp) : 0.0f);
