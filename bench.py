@@ -688,7 +688,9 @@ def main():
     # dispatch and release, ~2-4 us)
     per = {}
     guided_each = [f"fakequant_guided@{t}" for t in range(len(pairs))] if len(pairs) > 1 else [ROOF]
-    for nm in KERNELS + guided_each:
+    floor_each = [f"{nm}@{t}" for t, one in enumerate(onepass) if one
+                  for nm in ("rollout_onepass", "rtn_onepass", "amax_rollout")]
+    for nm in KERNELS + guided_each + floor_each:
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(K):
@@ -716,6 +718,43 @@ def main():
                     "GBps": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(bpe[nm] * n_total / (per[nm] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                for nm in KERNELS}
+
+    # Floor of the one-pass kernels per tensor that runs them: the input read
+    # once (the amax kernel on the same tensor: a read of it and little else)
+    # plus the outputs written once (a write-only fill of the same number of
+    # bytes, torch's fill kernel), one after the other, since no block can be
+    # written before the whole group has been read.
+    def fill_us(nbytes):
+        bufw = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+        for i in range(4):
+            bufw[i % 2].fill_(i)
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(K):
+            bufw[i % 2].fill_(i & 255)
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / K * 1e3
+
+    floors = {}
+    for t, one in enumerate(onepass):
+        if not one:
+            continue
+        n_t = ns[t]
+        rd = per[f"amax_rollout@{t}"] * 1e3
+        lines = {}
+        for nm, out_b, bpe_nm in (("rollout_onepass", n_t * (0.5 + 1 / 16 + 1 / 16 + k / 8), "rollout_onepass"),
+                                  ("rtn_onepass", 2 * n_t, "rtn_onepass")):
+            wr = fill_us(int(out_b))
+            us = per[f"{nm}@{t}"] * 1e3
+            alg = bpe[bpe_nm] * n_t
+            lines[nm] = {"us": round(us, 2), "frac_of_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "read_floor_us": round(rd, 2), "write_floor_us": round(wr, 2),
+                         "floor_us": round(rd + wr, 2),
+                         "floor_frac_of_peak": round(alg / ((rd + wr) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "kernel_over_floor": round(us / (rd + wr), 3)}
+        floors[f"{names_shapes[t][0]} {'x'.join(map(str, names_shapes[t][1]))} G={Gs[t]}"] = lines
 
     if args.calib_copy_mib:
         m = args.calib_copy_mib << 20
@@ -798,6 +837,7 @@ def main():
                                f"{'x'.join(map(str, names_shapes[0][1]))}",
                      "algorithmic_bytes_per_launch": int(g_bytes), "avg_launch_us": round(g_ms * 1e3, 2)},
         "guided_fakequant": guided,
+        "onepass_floor": floors,
         "copy_reference": {"GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
                            "what": "torch copy_ of a 256 MiB buffer on the same GPU in the same run (runtime blit "
                                    "kernel), read + write bytes"},
