@@ -128,7 +128,7 @@ int trace_quant_weight(const void *w_bf16, int64_t n, int G, float *g_out, uint8
 int trace_quant_rollout(const void *y_bf16, int64_t n, int G, const float *g, int k,
                         uint8_t *codes, uint8_t *scales, uint8_t *guidance, void *stream);
 
-/* Bytes of the work buffer of trace_quant_rollout_onepass: 8704 + 4 G,
+/* Bytes of the work buffer of trace_quant_rollout_onepass: 25 088 + 4 G,
  * rounded up to a multiple of 256 (0 if G < 1). */
 size_t trace_onepass_work_bytes(int G);
 
@@ -137,7 +137,9 @@ size_t trace_onepass_work_bytes(int G);
  * tensors up to this size (with G > 1, each group counted in whole tiles of
  * 8192 elements) are one launch that reads the input once.  A larger tensor
  * with G > 1 whose groups each fit runs one launch per block of whole groups
- * that fits, and is still read once.  Otherwise (G = 1, or a group larger
+ * that fits (in one launch, by teams of workgroups, when every group is a
+ * whole number of tiles and at least two such teams fit), and is still read
+ * once.  Otherwise (G = 1, or a group larger
  * than this) the excess is read twice and the two-kernel path (trace_amax +
  * trace_quant_rollout) is usually faster.  0 on error (no device,
  * max_workgroups < 0). */
@@ -175,7 +177,9 @@ int64_t trace_onepass_capacity(int max_workgroups);
  * Enqueues one kernel, or one per block of groups when the tensor exceeds
  * trace_onepass_capacity and its groups fit (see there); every launch writes
  * its groups' parts of the same output planes and leaves the work buffer
- * zeroed for the next. */
+ * zeroed for the next.  In the launch by teams, each team of workgroups takes
+ * its groups in turn and meets at a barrier of its own per group (bounded by
+ * the same time limit), so teams do not wait for one another. */
 int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
                                 uint8_t *scales, uint8_t *guidance, void *work, int max_workgroups,
                                 int *status_dev, void *stream);
@@ -183,7 +187,7 @@ int trace_quant_rollout_onepass(const void *y_bf16, int64_t n, int G, int k, flo
 /* The same one-pass rollout for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no work-buffer argument; its work buffer is a static array of
- * the library, 25 088 bytes per device (barrier counters and up to 4096
+ * the library, 41 472 bytes per device (barrier counters and up to 4096
  * group maxima), held by each device the library runs on until the process
  * ends.  The first call on a device looks up that device's copy and enqueues
  * one clear of it on `stream` before its launch; every call leaves it zeroed

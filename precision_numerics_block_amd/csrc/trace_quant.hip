@@ -838,7 +838,14 @@ constexpr uint32_t kOpLine = TRACE_OP_LINE_WORDS;
 constexpr uint32_t kOpSubgroups = 16;
 constexpr uint32_t kOpTopWord = kOpSubgroups * kOpLine;
 constexpr uint32_t kOpDoneWord = (kOpSubgroups + 1) * kOpLine;      // the same tree again, for departures
-constexpr uint32_t kOpAccWord = 2 * (kOpSubgroups + 1) * kOpLine;
+// Arrival counters of the teams of k_quant_onepass_teams, one line each.
+constexpr uint32_t kOpMaxTeams = 64;
+// Register tiles of k_quant_onepass_teams: its loop over groups keeps a few
+// more values live than k_quant_onepass, and 24 tiles spill (23 with f32
+// fake-quant output).
+constexpr int ot_reg_tiles(int out) { return out == 2 ? 22 : 23; }
+constexpr uint32_t kOpTeamWord = 2 * (kOpSubgroups + 1) * kOpLine;
+constexpr uint32_t kOpAccWord = kOpTeamWord + kOpMaxTeams * kOpLine;
 constexpr int kOpGroupSlots = 128;                 // global scales a workgroup keeps in LDS
 constexpr uint32_t kOpTabSlots = 4;                // groups with scale tables, several-group rollout
 
@@ -846,7 +853,7 @@ constexpr uint32_t kOpTabSlots = 4;                // groups with scale tables, 
 // (barrier trees and group maxima, the layout above) is the static array
 // `scratch` below, one copy per device.
 constexpr int kScratchMaxGroups = 4096;
-constexpr uint32_t kScratchWords = kOpAccWord + kScratchMaxGroups;   // 25 088 bytes
+constexpr uint32_t kScratchWords = kOpAccWord + kScratchMaxGroups;   // 41 472 bytes
 
 }  // namespace
 
@@ -870,6 +877,7 @@ struct OnePass {
     uint32_t *codes;        // rollout codes, or the fake-quant's chosen codes (nullable there)
     uint8_t *scales, *gd_scales, *gd_bits;
     void *out;              // fake-quant output (bf16 or f32), else null
+    uint32_t team_size;     // k_quant_onepass_teams: workgroups per team
 };
 
 // Where the chunks of item it lie (all uniform): chunk u of thread t is
@@ -1436,6 +1444,184 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     __syncthreads();
     if (leaving_last) {
         for (uint32_t i = threadIdx.x; i < 2 * (kOpSubgroups + 1); i += kOpThreads)
+            a.work[i * kOpLine] = 0u;
+        for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
+            a.work[kOpAccWord + i] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One-pass over many groups in teams of workgroups.
+//
+// When every group is a whole number of tiles and the tensor exceeds the
+// on-chip capacity but a group takes only part of the chip, the grid is cut
+// into T teams of S workgroups (S the fewest that hold one group on chip).
+// Team t takes groups t, t + T, t + 2T, ... in turn.  For each group the
+// team's members split its tiles evenly, hold their share on chip (LDS tiles
+// first, register tiles last) as k_quant_onepass holds a run, publish the
+// group's maximum, and meet at a barrier of their team alone (one counter
+// line per team, counted up over the rounds: round r is complete at
+// (r + 1) S arrivals); then they convert and store, and go on to the team's
+// next group.  The input is read once; no barrier spans the grid, so the
+// teams drift apart: one team's stores overlap another team's reads, and a
+// slow workgroup holds up only its own team.  Registers and LDS are free at
+// the end of each round.
+// After a barrier times out the workgroup stops working, still arrives at
+// its team's remaining rounds without waiting, and counts out, so every
+// workgroup exits and the last one out leaves the work buffer zeroed.
+// ---------------------------------------------------------------------------
+template <int K, int OUT, bool kTab>
+__global__ void __launch_bounds__(kOpThreads) k_quant_onepass_teams(OnePass a)
+{
+    static_assert(!kTab || OUT == 0, "scale tables serve the rollout codes only");
+    constexpr int kOtRegTiles = ot_reg_tiles(OUT);
+    extern __shared__ u32x4 lds_tiles[];               // a.lds_tiles * 2 * kOpThreads chunks
+    __shared__ uint32_t wmax[kOpThreads / 64];
+    __shared__ int passed;
+    __shared__ bool leaving_last;
+    __shared__ float gshared;
+    __shared__ float2 stab[kTab ? 256 : 1];
+    __shared__ float ctab[kTab ? 128 : 1];
+    __shared__ int ktab;
+
+    const uint32_t S = a.team_size, T = gridDim.x / S;     // the host launches T * S workgroups
+    const uint32_t team = blockIdx.x / S, member = blockIdx.x - team * S;
+    uint32_t *counter = a.work + kOpTeamWord + team * kOpLine;
+    if (threadIdx.x == 0)
+        passed = 1;
+    __syncthreads();
+    uint32_t round = 0;
+    for (uint32_t grp = team; grp < a.G; grp += T, ++round) {
+        // this member's share of the group: items [i0, i0 + cnt), at most
+        // kOtRegTiles + a.lds_tiles (the host's choice of S)
+        const uint32_t base = grp * a.tpg;
+        const uint32_t i0 = base + (uint32_t)((uint64_t)a.tpg * member / S);
+        const uint32_t cnt = base + (uint32_t)((uint64_t)a.tpg * (member + 1) / S) - i0;
+        const uint32_t nreg = min(cnt, (uint32_t)kOtRegTiles);
+        const uint32_t nlds = cnt - nreg;
+        const uint32_t i_reg = i0 + nlds;
+        Blk hr[kOtRegTiles];
+        uint32_t hab[kOtRegTiles];
+        if (passed) {
+            // ---- phase 1: read the share once, fold its maximum -----------------
+            for (uint32_t j = 0; j < nlds; ++j)
+                load_item_to_lds(a, item_at<false>(a, i0 + j), lds_tiles, j);
+#pragma unroll
+            for (int h = 0; h < kOtRegTiles; ++h) {
+                Chunk x[2];
+                load_item(a, item_at<false>(a, i_reg + h), (uint32_t)h < nreg, x);
+                hr[h].lo = x[0];
+                hr[h].hi = x[1];
+            }
+            __builtin_amdgcn_s_waitcnt(0);             // the LDS copies have landed (this wave's own)
+            uint32_t run = 0;
+            for (uint32_t j = 0; j < nlds; ++j) {
+                Chunk x[2];
+                read_item_from_lds(lds_tiles, item_at<false>(a, i0 + j), j, x);
+                run = max(run, max(chunk_amax_finite(x[0], a.status), chunk_amax_finite(x[1], a.status)));
+            }
+#pragma unroll
+            for (int h = 0; h < kOtRegTiles; ++h) {
+                Chunk x[2] = {hr[h].lo, hr[h].hi};
+                hr[h] = to_block(x);
+                hab[h] = block_amax_bits(hr[h]);
+                if ((uint32_t)h < nreg)
+                    run = max(run, hab[h] < 0x7f80u ? hab[h]
+                                                    : max(chunk_amax_finite(hr[h].lo, a.status),
+                                                          chunk_amax_finite(hr[h].hi, a.status)));
+            }
+            if (cnt > 0)
+                amax_publish<kOpThreads, true>(run, wmax, a.work + kOpAccWord + grp);
+        }
+
+        // ---- the team's barrier for this group (bounded) ----------------------
+        // Every maximum this workgroup published has been performed before it
+        // arrives; the group maximum is read back with a device-scope load.
+        if (threadIdx.x == 0) {
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (passed) {
+                const uint32_t target = (round + 1) * S;
+                const uint64_t t0 = (uint64_t)wall_clock64();
+                while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                    __builtin_amdgcn_s_sleep(8);
+                    if ((uint64_t)wall_clock64() - t0 > a.wait_ticks) {
+                        passed = 0;                    // outputs undefined from here on
+                        if (a.status)
+                            *a.status = TRACE_E_BARRIER;
+                        break;
+                    }
+                }
+                if (passed)
+                    gshared = as_f(group_amax_bits(a, grp)) / 2688.0f;
+            }
+        }
+        __syncthreads();
+        if (!passed)
+            continue;                                  // arrive at the remaining rounds only
+
+        // ---- phase 2: convert and store the share ------------------------------
+        // (item positions from copies the compiler cannot see through, so the
+        // scalar values of phase 1 are not kept alive across the barrier)
+        uint32_t p2_i0 = i0, p2_reg = i_reg, p2_cnt = cnt;
+        asm volatile("" : "+s"(p2_i0), "+s"(p2_reg), "+s"(p2_cnt));
+        const float gv = gshared;
+        if constexpr (kTab) {
+            for (uint32_t e = threadIdx.x; e < 384u; e += kOpThreads) {
+                if (e < 256u)
+                    stab[e] = scale_table_entry(e, gv);
+                else
+                    ctab[e - 256u] = inv_combined(e4m3_decode(e - 256u), gv);
+            }
+            if (threadIdx.x == 0)
+                ktab = scale_table_k(gv);
+            __syncthreads();
+        }
+        if (member == 0 && threadIdx.x == 0)
+            a.g_out[grp] = gv;
+        if (blockIdx.x == 0 && round == 0 && a.gd_scales)
+            zero_pad<kOpThreads>(a.gd_scales, a.pad_begin, a.pad_end);
+        const GroupTabs tabs{stab, ctab, kTab ? __builtin_amdgcn_readfirstlane(ktab) : 0};
+        // one descriptor per output over the share (whole tiles); register
+        // tiles past the share lie outside its records and store nothing
+        const Outs span = outs_over<K, OUT>(a, item_at<false>(a, p2_i0).first, p2_cnt * (uint32_t)kOpTile);
+        if constexpr (kTab) {
+            // the next tile's two dependent table reads are issued before this
+            // tile's conversion and stores (as in k_quant_onepass)
+            ScInv nx = block_scale_inv<true>(hab[0], 0.0f, tabs);
+#pragma unroll
+            for (int h = 0; h < kOtRegTiles; ++h) {
+                const ScInv cur = nx;
+                if (h + 1 < kOtRegTiles)
+                    nx = block_scale_inv<true>(hab[h + 1], 0.0f, tabs);
+                quant_block_with<K>(span, item_at<false>(a, p2_reg + h), hr[h], cur);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < kOtRegTiles; ++h) {
+                const Item w = item_at<false>(a, p2_reg + h);
+                if constexpr (OUT == 0)
+                    quant_block<K, false>(span, w, hr[h], hab[h], gv, tabs);
+                else
+                    rtn_block<OUT>(span, w, hr[h], hab[h], gv);
+            }
+        }
+        for (uint32_t j = 0; j < p2_reg - p2_i0; ++j) {
+            const Item w = item_at<false>(a, p2_i0 + j);
+            const Blk b = block_from_lds(lds_tiles, j);
+            if constexpr (OUT == 0)
+                quant_block<K, kTab>(span, w, b, block_amax_bits(b), gv, tabs);
+            else
+                rtn_block<OUT>(span, w, b, block_amax_bits(b), gv);
+        }
+    }
+
+    // ---- departure, as in k_quant_onepass (the team lines cleared too) -------
+    __syncthreads();
+    if (threadIdx.x == 0)
+        tree_count(a.work + kOpDoneWord, gridDim.x, &leaving_last);
+    __syncthreads();
+    if (leaving_last) {
+        for (uint32_t i = threadIdx.x; i < 2 * (kOpSubgroups + 1) + kOpMaxTeams; i += kOpThreads)
             a.work[i * kOpLine] = 0u;
         for (uint32_t i = threadIdx.x; i < a.G; i += kOpThreads)
             a.work[kOpAccWord + i] = 0u;
@@ -2224,6 +2410,86 @@ int rtn_onepass_launch(const void *x_bf16, int64_t n, int G, float *g_out, void 
     return launched();
 }
 
+// Team shape for k_quant_onepass_teams: S workgroups per team (the fewest
+// that hold one group on chip) and the grid T * S, or false when it does not
+// apply.  It applies when a call would otherwise take several launches
+// (gpb < G), every group is a whole number of tiles, and at least two teams
+// fit in the grid (at most kOpMaxTeams, each on its own counter line).
+bool onepass_team_shape(int64_t n, int G, int gpb, int max_workgroups, int out, uint32_t &S, int64_t &grid)
+{
+    OnePassDevice d;
+    if (gpb >= G || (n / 8 / G) % kOpTile != 0 || onepass_device(d) != TRACE_OK)
+        return false;
+    int64_t cap = (int64_t)d.cus * d.per_cu;
+    if (max_workgroups > 0 && max_workgroups < cap)
+        cap = max_workgroups;
+    const int64_t tpg = n / 8 / G / kOpTile;
+    const int64_t per_wg = ot_reg_tiles(out) + (int64_t)d.lds_tiles;
+    const int64_t size = (tpg + per_wg - 1) / per_wg;
+    const int64_t teams = std::min<int64_t>({cap / size, (int64_t)kOpMaxTeams, (int64_t)G});
+    if (teams < 2)
+        return false;
+    S = (uint32_t)size;
+    grid = teams * size;
+    return true;
+}
+
+int rollout_onepass_teams(const void *y_bf16, int64_t n, int G, int k, float *g_out, uint8_t *codes,
+                          uint8_t *scales, uint8_t *guidance, void *work, uint32_t S, int64_t grid_teams,
+                          int *status_dev, hipStream_t st)
+{
+    OnePass a;
+    int64_t grid;
+    size_t lds;
+    int rc = onepass_plan(y_bf16, n, G, g_out, work, (int)grid_teams, status_dev, 4u, a, grid, lds);
+    if (rc != TRACE_OK)
+        return rc;
+    if (grid != grid_teams)                            // the plan keeps the grid asked for (it is below the cap)
+        return TRACE_E_HIP;
+    a.team_size = S;
+    a.codes = (uint32_t *)codes;
+    a.scales = scales;
+    a.gd_scales = guidance;
+    a.gd_bits = guidance ? guidance + bitplane_offset(n) : nullptr;
+    (void)hipGetLastError();
+#define TRACE_OT(KK) \
+    hipLaunchKernelGGL((k_quant_onepass_teams<KK, 0, true>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a)
+    if (k == 1)
+        TRACE_OT(1);
+    else if (k == 2)
+        TRACE_OT(2);
+    else if (k == 3)
+        TRACE_OT(3);
+    else
+        TRACE_OT(4);
+#undef TRACE_OT
+    return launched();
+}
+
+int rtn_onepass_teams(const void *x_bf16, int64_t n, int G, float *g_out, void *y_out, bool f32, uint8_t *codes_out,
+                      uint8_t *scales_out, void *work, uint32_t S, int64_t grid_teams, int *status_dev,
+                      hipStream_t st)
+{
+    OnePass a;
+    int64_t grid;
+    size_t lds;
+    int rc = onepass_plan(x_bf16, n, G, g_out, work, (int)grid_teams, status_dev, f32 ? 32u : 16u, a, grid, lds);
+    if (rc != TRACE_OK)
+        return rc;
+    if (grid != grid_teams)
+        return TRACE_E_HIP;
+    a.team_size = S;
+    a.codes = (uint32_t *)codes_out;
+    a.scales = scales_out;
+    a.out = y_out;
+    (void)hipGetLastError();
+    if (f32)
+        hipLaunchKernelGGL((k_quant_onepass_teams<2, 2, false>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_quant_onepass_teams<2, 1, false>), dim3((uint32_t)grid), dim3(kOpThreads), lds, st, a);
+    return launched();
+}
+
 // Argument checks of the one-pass rollout entry points (with or without a
 // caller-owned work buffer), before anything touches the device.
 int rollout_onepass_check(const void *y_bf16, int64_t n, int G, int k, const float *g_out, const uint8_t *codes,
@@ -2253,6 +2519,10 @@ int rollout_onepass_run(const void *y_bf16, int64_t n, int G, int k, float *g_ou
     int gpb, rc;
     if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
         return rc;
+    uint32_t S;
+    int64_t grid;
+    if (onepass_team_shape(n, G, gpb, max_workgroups, 0, S, grid))   // many groups of whole tiles: one launch in teams
+        return rollout_onepass_teams(y_bf16, n, G, k, g_out, codes, scales, guidance, work, S, grid, status_dev, st);
     const int64_t per = n / G, bits = bitplane_offset(n);
     for (int g0 = 0; g0 < G; g0 += gpb) {              // blocks of whole groups (one block when it all fits)
         const int gb = std::min(gpb, G - g0);
@@ -2356,6 +2626,11 @@ int trace_fakequant_rtn_onepass(const void *x_bf16, int64_t n, int G, float *g_o
     if ((rc = onepass_groups_per_launch(n, G, max_workgroups, gpb)) != TRACE_OK)
         return rc;
     const bool f32 = out_dtype == TRACE_OUT_F32;
+    uint32_t S;
+    int64_t grid;
+    if (onepass_team_shape(n, G, gpb, max_workgroups, f32 ? 2 : 1, S, grid))   // many groups of whole tiles: teams
+        return rtn_onepass_teams(x_bf16, n, G, g_out, y_out, f32, codes_out, scales_out, work, S, grid, status_dev,
+                                 (hipStream_t)stream);
     const int64_t per = n / G;
     for (int g0 = 0; g0 < G; g0 += gpb) {              // blocks of whole groups (one block when it all fits)
         const int gb = std::min(gpb, G - g0);

@@ -52,8 +52,8 @@ def test_sizes(tq):
     assert tq.code_bytes(17) == 0 and tq.code_bytes(0) == 0
     assert tq.version() >= 100
     assert tq.lib.trace_status_str(-7).decode().startswith("an input")
-    assert tq.onepass_work_bytes(1) == 8960 and tq.onepass_work_bytes(64) == 8960
-    assert tq.onepass_work_bytes(65) == 9216 and tq.onepass_work_bytes(0) == 0
+    assert tq.onepass_work_bytes(1) == 25344 and tq.onepass_work_bytes(64) == 25344
+    assert tq.onepass_work_bytes(65) == 25600 and tq.onepass_work_bytes(0) == 0
     assert "barrier" in tq.lib.trace_status_str(-10).decode()
     assert "4096" in tq.lib.trace_status_str(-11).decode()
     assert "2^34" in tq.lib.trace_status_str(-2).decode()

@@ -169,7 +169,8 @@ def test_full_size_every_element(tq, wl):
 def test_full_size_per_expert_scales(tq):
     """The batched MoE step's activations with one global scale per expert
     (G = 128, the bench's per-expert line): the one-pass entry points in one
-    launch per block of experts, every element against the oracle."""
+    launch by teams of workgroups (each team holds one expert's activations
+    on chip at a time), every element against the oracle."""
     (name, shape), = synth.tensor_specs(5)[:1]
     X, Y = synth.make_pair(5, 0, shape, DEV)
     G = shape[0]

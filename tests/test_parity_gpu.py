@@ -747,6 +747,13 @@ GROUP_BLOCKS = [
     ("act", 2, 4, 5, (1, 2, 3, 4)),      # 165 on chip: 2 launches of two groups
     ("act", 2, 8, 3, (1, 2, 3, 4)),      # 32-tile groups, 99 on chip: launches of 3, 3 and 2 groups
     ("ragged", 3 * 7001, 3, 1, (1, 2, 3, 4)),   # 14-tile groups (last tile short): launches of 2 and 1
+    # one launch by teams of workgroups (groups of whole tiles, a team holds a
+    # group on chip, at least two teams under the cap; 32 tiles per workgroup
+    # on MI355X, 31 with f32 output):
+    ("act", 4, 8, 8, (1, 2, 3, 4)),      # 64-tile groups: 4 teams of 2, two groups each (f32: 2 teams of 3)
+    ("act", 3, 4, 7, (2,)),              # 96-tile groups: 2 teams of 3, LDS tiles in use (f32: launches)
+    ("ragged", 5 * 37 * 512, 5, 4, (1, 2, 3, 4)),   # random data, 37-tile groups: shares of 18 and 19 tiles,
+                                                    # team 0 takes three groups, team 1 two
 ]
 
 
@@ -940,6 +947,42 @@ def test_onepass_barrier_timeout_reported(tq, monkeypatch):
     assert int(st[0]) == 0 and bool((work == 0).all())
     ogx, _ = oracle.amax(h16(X))
     oy, _, _ = oracle.fakequant_rtn(h16(X), ogx, None, 1, False)
+    assert_eq(gx.cpu().numpy().view(np.uint32), ogx.view(np.uint32), "rtn g")
+    assert_eq(h16(y), oy, "rtn y")
+
+
+def test_onepass_teams_barrier_timeout_reported(tq, monkeypatch):
+    """The failure path of the per-team barriers of the launch by teams
+    (8 groups of 64 tiles under a cap of 8 workgroups: 4 teams of 2, two
+    rounds each), forced from the host with a zero time limit: the status
+    word reports TRACE_E_BARRIER, every kernel exits, the work buffer comes
+    back zeroed, and the next calls on it (rollout and own-scale RTN) are
+    exact against the oracle."""
+    X, Y = synth.make_pair(2, 0, (4, 512, 2048), DEV)
+    G, cap = 8, 8
+    work = torch.zeros(tq.onepass_work_bytes(G), dtype=torch.uint8, device=DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    monkeypatch.setenv("TRACE_ONEPASS_WAIT_US", "0")
+    tq.quant_rollout_onepass(Y, 2, G, status=st, work=work, max_workgroups=cap)
+    tq.fakequant_rtn_onepass(X, G, status=st, work=work, max_workgroups=cap)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -10
+    assert bool((work == 0).all()), "timed-out calls leave the work buffer zeroed"
+    monkeypatch.delenv("TRACE_ONEPASS_WAIT_US")
+    st.zero_()
+    g, codes, scales, gd = tq.quant_rollout_onepass(Y, 2, G, status=st, work=work, max_workgroups=cap)
+    gx, y, _, _ = tq.fakequant_rtn_onepass(X, G, status=st, work=work, max_workgroups=cap)
+    torch.cuda.synchronize()
+    assert int(st[0]) == 0 and bool((work == 0).all())
+    Yh, Xh = h16(Y), h16(X)
+    og, _ = oracle.amax(Yh, G)
+    oc, os_, ogd = oracle.quant_rollout(Yh, og, 2, G)
+    assert_eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), "g")
+    assert_eq(h8(codes), oc, "codes")
+    assert_eq(h8(scales), os_, "scales")
+    assert_eq(h8(gd), ogd, "guidance")
+    ogx, _ = oracle.amax(Xh, G)
+    oy, _, _ = oracle.fakequant_rtn(Xh, ogx, None, G, False)
     assert_eq(gx.cpu().numpy().view(np.uint32), ogx.view(np.uint32), "rtn g")
     assert_eq(h16(y), oy, "rtn y")
 
