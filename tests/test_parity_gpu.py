@@ -754,6 +754,8 @@ GROUP_BLOCKS = [
     ("act", 3, 4, 7, (2,)),              # 96-tile groups: 2 teams of 3, LDS tiles in use (f32: launches)
     ("ragged", 5 * 37 * 512, 5, 4, (1, 2, 3, 4)),   # random data, 37-tile groups: shares of 18 and 19 tiles,
                                                     # team 0 takes three groups, team 1 two
+    ("ragged", 300 * 512, 300, 8, (2,)),            # one-tile groups: 8 teams of one, 38 rounds (the last short)
+    ("ragged", 2400 * 512, 2400, 70, (1, 4)),       # 64 teams (every team line in use), 38 rounds
 ]
 
 
