@@ -28,7 +28,7 @@
 //   * the guided decision is one fp32 compare against a threshold read from
 //     a small LDS table indexed by (bucket of |v|, guidance value): chosen
 //     index = floor index + (|v| > threshold);
-//   * streaming kernels launch one tile of 256 x kUnroll chunks per
+//   * streaming kernels launch one tile of 128 x kUnroll chunks per
 //     workgroup (many small workgroups balance best across the 8 XCDs).
 #include <hip/hip_runtime.h>
 
@@ -86,7 +86,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 
-constexpr int kThreads = 256;          // 4 wavefronts of 64
+constexpr int kThreads = 128;          // 2 wavefronts of 64
 constexpr int kUnroll = TRACE_UNROLL;  // chunks per thread per tile
 constexpr int kTile = kThreads * kUnroll;
 constexpr int kMaxGrid = TRACE_WG_PER_CU > 0 ? 256 * TRACE_WG_PER_CU : 0x7fffffff;
