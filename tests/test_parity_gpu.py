@@ -878,6 +878,68 @@ def test_onepass_nonfinite_flag_and_repeat(tq):
         assert_eq(h8(gd2), ogd, f"guidance G={G} cap={cap}")
 
 
+def test_onepass_teams_nonfinite_and_work_reuse(tq):
+    """The launch by teams (8 groups of 64 tiles under a cap of 8 workgroups:
+    4 teams of 2, two rounds each) on input with an inf and a NaN in two
+    groups of different teams and rounds (one in an LDS tile, one in a
+    register tile): the status word reports TRACE_E_NONFINITE and the global
+    scales equal the oracle's (which skips non-finite values in the group
+    maxima).  Non-finite inputs are outside the contract, so the outputs of
+    the two blocks that hold them are left unchecked; every other byte must
+    equal the oracle's.  The same work buffer then serves a one-launch call
+    and the launch by teams again, each exact."""
+    G, cap = 8, 8
+    X, Y = synth.make_pair(2, 0, (4, 512, 2048), DEV)
+    n = Y.numel()
+    per = n // G
+    bad_el = (1 * per + 123, 6 * per + 4567 + 16 * 512 * 30)   # LDS tile 0, register tile 30 (member 0)
+    yb = Y.reshape(-1).clone()
+    yb[bad_el[0]] = float("inf")
+    yb[bad_el[1]] = float("nan")
+    bad_blk = [e // 16 for e in bad_el]
+
+    def keep(nbytes, per_block):
+        m = np.ones(nbytes, bool)
+        for b in bad_blk:
+            m[b * per_block:(b + 1) * per_block] = False
+        return m
+
+    work = torch.zeros(tq.onepass_work_bytes(G), dtype=torch.uint8, device=DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    for Yc, Gc, capc, flag in ((yb.view_as(Y), G, cap, -7), (Y, 2, 0, 0), (Y, G, cap, 0)):
+        st.zero_()
+        g, codes, scales, gd = tq.quant_rollout_onepass(Yc, 2, Gc, status=st, work=work, max_workgroups=capc)
+        torch.cuda.synchronize()
+        assert int(st[0]) == flag
+        assert bool((work == 0).all()), "the call leaves its work buffer zeroed"
+        Yh = h16(Yc)
+        og, _ = oracle.amax(Yh, Gc)
+        oc, os_, ogd = oracle.quant_rollout(Yh, og, 2, Gc)
+        what = f"G={Gc} cap={capc}"
+        assert_eq(g.cpu().numpy().view(np.uint32), og.view(np.uint32), f"g {what}")
+        mc, ms = keep(n // 2, 8), keep(n // 16, 1)
+        bits0 = tq.guidance_bytes(n, 2) - n // 4
+        mg = np.concatenate([ms, np.ones(bits0 - n // 16, bool), keep(n // 4, 4)])
+        if flag == 0:
+            mc[:], ms[:], mg[:] = True, True, True
+        assert_eq(h8(codes)[mc], oc[mc], f"codes {what}")
+        assert_eq(h8(scales)[ms], os_[ms], f"scales {what}")
+        assert_eq(h8(gd)[mg], ogd[mg], f"guidance {what}")
+    xb = X.reshape(-1).clone()
+    xb[bad_el[0]] = float("-inf")
+    st.zero_()
+    gx, y, _, _ = tq.fakequant_rtn_onepass(xb.view_as(X), G, status=st, work=work, max_workgroups=cap)
+    torch.cuda.synchronize()
+    assert int(st[0]) == -7 and bool((work == 0).all())
+    Xh = h16(xb)
+    ogx, _ = oracle.amax(Xh, G)
+    oy, _, _ = oracle.fakequant_rtn(Xh, ogx, None, G, False)
+    assert_eq(gx.cpu().numpy().view(np.uint32), ogx.view(np.uint32), "rtn g")
+    my = keep(n, 16)
+    my[bad_blk[1] * 16:(bad_blk[1] + 1) * 16] = True       # only the first block holds a non-finite x here
+    assert_eq(h16(y)[my], oy[my], "rtn y")
+
+
 def test_onepass_graph_replay_matches_eager(tq):
     X, Y = synth.make_pair(2, 0, (4, 512, 2048), DEV)
     n = Y.numel()
