@@ -16,18 +16,28 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose=False):
+# The measurement build of the one-pass phase clocks (phase_clock.py): the
+# same sources and flags with TRACE_OP_PHASE_CLOCK=1.  Not the product library.
+OUT_PHASE_CLOCK = os.path.join(HERE, "libtrace_quant_phaseclock.so")
+
+
+def build(verbose=False, out=OUT, defines=()):
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", os.path.join(ROOT, "include"), *SRCS,
+           "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed: " + " ".join(cmd))
     if verbose:
         sys.stderr.write(res.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
+
+
+def build_phase_clock(verbose=False):
+    return build(verbose, OUT_PHASE_CLOCK, ("TRACE_OP_PHASE_CLOCK=1",))
 
 
 if __name__ == "__main__":

@@ -29,7 +29,12 @@
 //     a small LDS table indexed by (bucket of |v|, guidance value): chosen
 //     index = floor index + (|v| > threshold);
 //   * streaming kernels launch one tile of 128 x kUnroll chunks per
-//     workgroup (many small workgroups balance best across the 8 XCDs).
+//     workgroup (many small workgroups balance best across the 8 XCDs);
+//   * the one-pass kernels (amax and quantise from one read) run one
+//     persistent 512-thread workgroup per compute unit that holds its share
+//     of the tensor on chip (registers and LDS) across a bounded grid
+//     barrier; many groups beyond the chip's capacity run in teams of
+//     workgroups, each team with a barrier of its own per group.
 #include <hip/hip_runtime.h>
 
 #include <bit>
@@ -51,7 +56,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Launch shape and cache hints (fixed at build time; the values below are the
-// measured best on MI355X for the 64x512x2048 activation workload).
+// measured best on MI355X for the 64x512x2048 activations and the batched
+// MoE step of 128x1024x4096 activations plus a 2x65536x8x128 KV layer).
 #ifndef TRACE_UNROLL
 #define TRACE_UNROLL 2
 #endif
@@ -831,6 +837,14 @@ constexpr int kOpStream = 4;                       // tiles in flight per lane w
 // one top counter, each on its own 256-byte line (a same-address atomic costs
 // about 30 ns on MI355X, so 256 arrivals on one word serialise for ~8 us;
 // two levels of 16 take ~1 us), then the group amax bits.
+// Phase clocks of k_quant_onepass (a measurement build only: the product
+// library is built with 0 and carries none of it).  With 1, thread 0 of each
+// workgroup writes the wall clock at the kernel's start, at the end of phase
+// 1, when the grid barrier has passed and at the end of phase 2 into the
+// buffer set by trace_debug_phase_clock (4 values per workgroup).
+#ifndef TRACE_OP_PHASE_CLOCK
+#define TRACE_OP_PHASE_CLOCK 0
+#endif
 #ifndef TRACE_OP_LINE_WORDS
 #define TRACE_OP_LINE_WORDS 64
 #endif
@@ -878,7 +892,17 @@ struct OnePass {
     uint8_t *scales, *gd_scales, *gd_bits;
     void *out;              // fake-quant output (bf16 or f32), else null
     uint32_t team_size;     // k_quant_onepass_teams: workgroups per team
+    uint64_t *clock;        // phase clocks (TRACE_OP_PHASE_CLOCK builds), else null
 };
+
+// One phase stamp of k_quant_onepass (see TRACE_OP_PHASE_CLOCK).
+__device__ __forceinline__ void phase_stamp(const OnePass &a, uint32_t i)
+{
+    if constexpr (TRACE_OP_PHASE_CLOCK != 0) {
+        if (threadIdx.x == 0 && a.clock)
+            a.clock[blockIdx.x * 4u + i] = (uint64_t)wall_clock64();
+    }
+}
 
 // Where the chunks of item it lie (all uniform): chunk u of thread t is
 // first + u * T + t, so each load is 16 bytes per lane, contiguous across the
@@ -1202,6 +1226,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     __shared__ float ctab[kTab ? kSlots * 128 : 1];    // 1 / (s * g) per scale code, per slot
     __shared__ int ktab[kTab ? kSlots : 1];
 
+    phase_stamp(a, 0);
     const uint32_t P = gridDim.x;
     const uint32_t i0 = (uint32_t)((uint64_t)a.items * blockIdx.x / P);
     const uint32_t cnt = (uint32_t)((uint64_t)a.items * (blockIdx.x + 1) / P) - i0;
@@ -1272,6 +1297,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     }
     if (cnt > 0)
         amax_publish<kOpThreads, true>(run, wmax, acc + cur);
+    phase_stamp(a, 1);
 
     // ---- grid barrier ------------------------------------------------------
     // Bounded: a launch whose workgroups are not all resident gives up after
@@ -1301,6 +1327,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
         passed = ok;
     }
     __syncthreads();
+    phase_stamp(a, 2);
     if (!passed) {
         // Outputs are undefined.  This workgroup still counts out below, as
         // every workgroup does (also one that arrives after the others gave
@@ -1439,6 +1466,7 @@ __global__ void __launch_bounds__(kOpThreads) k_quant_onepass(OnePass a)
     // work buffer, so nothing reads the words the last one clears; the next
     // call on the stream starts after this kernel has finished.
     __syncthreads();
+    phase_stamp(a, 3);
     if (threadIdx.x == 0)
         tree_count(a.work + kOpDoneWord, P, &leaving_last);
     __syncthreads();
@@ -2252,6 +2280,10 @@ bool onepass_cap_fits(int64_t n, int G, int max_workgroups, uint32_t bytes_per_c
     return onepass_run_fits(items, max_workgroups, bytes_per_chunk);
 }
 
+#if TRACE_OP_PHASE_CLOCK
+uint64_t *g_phase_clock = nullptr;   // device buffer of 4 values per workgroup, set by trace_debug_phase_clock
+#endif
+
 // The launch parameters shared by both one-pass entry points (arguments
 // already checked): the item layout, the barrier limit and the grid.
 int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work, int max_workgroups,
@@ -2282,6 +2314,9 @@ int onepass_plan(const void *in_bf16, int64_t n, int G, float *g_out, void *work
     a.work = (uint32_t *)work;
     a.g_out = g_out;
     a.status = status_dev;
+#if TRACE_OP_PHASE_CLOCK
+    a.clock = g_phase_clock;
+#endif
     grid = (int64_t)d.cus * d.per_cu;
     if (max_workgroups > 0 && max_workgroups < grid)
         grid = max_workgroups;
@@ -2988,5 +3023,18 @@ const char *trace_status_str(int status)
 }
 
 int trace_version(void) { return 500; }
+
+#if TRACE_OP_PHASE_CLOCK
+// Measurement build only: where k_quant_onepass writes its phase clocks (a
+// device buffer of 4 values per workgroup, or null to stop).  Returns the
+// wall clock's rate on the current device in kHz (0 on error).  Not part of
+// the product library's interface.
+int trace_debug_phase_clock(void *dev_buf)
+{
+    g_phase_clock = static_cast<uint64_t *>(dev_buf);
+    OnePassDevice d;
+    return onepass_device(d) == TRACE_OK ? d.clock_khz : 0;
+}
+#endif
 
 }  // extern "C"
